@@ -1,0 +1,214 @@
+/*
+ * stepq.h -- C ABI of the MI355X (gfx950) quantized gated-delta state step.
+ *
+ * The library implements the decode-time hot path of STEPQuant (Yao et al.,
+ * 2026, "STEPQuant: When and Where Errors Matter in Delta-Rule Recurrent State
+ * Quantization"): every (request, layer, head) recurrent state S (d_k x d_v)
+ * lives in a packed pool as mixed-width integer codes with a binary16 factor
+ * per key row and a binary16 scale per value column, plus binary16 "pivot"
+ * rows kept unquantized.  One step dequantizes the state, applies the gated
+ * delta update, emits the readout y = X^T q from the float state, then refits
+ * the row factors and column scales and packs the state back.
+ *
+ * Passages the calls follow (STEPQuant pages):
+ *   - rcap.io post, decode-step pseudocode: unpack -> gated delta update ->
+ *     readout before requantization -> row scales sqrt(row_mag)/sqrt(impact)
+ *     -> weighted column fit -> quantize at each unit's width.
+ *   - hyper.ai summary, section 方法 (Method): lifetime-aware bit allocation and
+ *     FP16 pivot selection run offline; a fused kernel does chunked state
+ *     reconstruction, the delta update and the readout; the dual-axis fit and
+ *     packed write-back run on a separate stream, keeping the state compressed
+ *     between tokens.
+ *
+ * Conventions
+ *   - All sizes are element counts unless named *_bytes.
+ *   - "d_" prefixed pointers are device pointers (HIP device memory on the
+ *     current device); "h_" or unprefixed pointers in sq_plan_cfg are host.
+ *   - Streams are passed as void* and hold a hipStream_t (NULL = the null stream).
+ *   - Per-step arrays are laid out [n_layers][batch][H][d] (row-major, fp32).
+ *   - Every call validates its arguments on the host before enqueuing work and
+ *     returns a negative sq_status on failure, with a message available from
+ *     sq_last_error() on the calling thread.  Device work is asynchronous: a
+ *     device fault surfaces at the caller's next synchronization.  No C++
+ *     exception crosses this boundary.
+ */
+#ifndef STEPQ_H
+#define STEPQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sq_status;
+#define SQ_OK                 0
+#define SQ_ERR_ARG           -1   /* null pointer, bad enum, bad count */
+#define SQ_ERR_SHAPE         -2   /* sizes inconsistent with the plan or the buffer */
+#define SQ_ERR_UNSUPPORTED   -3   /* (d_k, d_v), width or grid size not compiled in */
+#define SQ_ERR_SLOT          -4   /* slot out of range or repeated (validate mode) */
+#define SQ_ERR_PLAN_MISMATCH -5   /* pool bound to another plan / layer range out of plan */
+#define SQ_ERR_NOMEM         -6   /* host or device allocation failed */
+#define SQ_ERR_HIP           -7   /* a HIP runtime call failed */
+
+#define SQ_FORM_GDN 0             /* one retention gate per head: D = alpha I        */
+#define SQ_FORM_KDA 1             /* one retention gate per key row: D = diag(alpha) */
+#define SQ_UNIT_HEAD 0            /* allocation unit: a whole head state             */
+#define SQ_UNIT_ROW  1            /* allocation unit: one key row of a head state    */
+
+#define SQ_MAX_WIDTHS 4
+#define SQ_MAX_GRID   8
+#define SQ_PIVOT_BITS 16          /* width reported for a pivot (binary16) unit/row  */
+
+/* Plan configuration (host memory; read during sq_plan_create only). */
+typedef struct sq_plan_cfg {
+    int32_t form;                 /* SQ_FORM_GDN or SQ_FORM_KDA */
+    int32_t unit;                 /* SQ_UNIT_HEAD or SQ_UNIT_ROW */
+    int32_t n_layers, n_heads, d_k, d_v;
+    int32_t n_widths;             /* candidate code widths, each in {4, 6, 8} */
+    int32_t widths[SQ_MAX_WIDTHS];
+    int32_t budget_milli;         /* average bits x 1000 over non-pivot units */
+    int32_t pivot_ppm;            /* pivot units: ceil(pivot_ppm * units / 1e6) */
+    int32_t n_grid;               /* column-scale candidates gamma (1..8), relative to the column base */
+    float   grid[SQ_MAX_GRID];
+    const float* gate;            /* alpha per unit for calibration: [L][H] (GDN) or [L][H][d_k] (KDA) */
+    const float* impact;          /* row-impact score w [L][H][d_k]; NULL = estimate from the traces */
+    const int32_t* unit_bits;     /* optional fixed allocation per unit (4/6/8, 16 = pivot); NULL = plan */
+    /* calibration traces; NULL q = draw them with the built-in Philox-4x32-10 generator */
+    const float* calib_q;         /* [L][H][S][T][d_k] */
+    const float* calib_k;         /* [L][H][S][T][d_k] */
+    const float* calib_v;         /* [L][H][S][T][d_v] */
+    const float* calib_beta;      /* [L][H][S][T] */
+    uint64_t calib_seed;
+    int32_t calib_segments;       /* S */
+    int32_t calib_len;            /* T */
+    int32_t n_threads;            /* planner threads; 0 = all hardware threads */
+} sq_plan_cfg;
+
+typedef struct sq_plan sq_plan;   /* host-side plan (opaque) */
+typedef struct sq_pool sq_pool;   /* a device pool bound to a plan (opaque) */
+
+/* Summary of a plan's layout. */
+typedef struct sq_plan_desc {
+    int32_t n_layers, n_heads, d_k, d_v, form, unit, n_units, n_pivot_units;
+    int32_t n_grid;
+    int32_t n_widths;
+    int32_t widths[SQ_MAX_WIDTHS];/* candidate widths, ascending */
+    uint64_t slot_bytes;          /* bytes of one slot (all layers and heads of one request) */
+    double code_bits_per_entry;   /* allocated bits per state entry, pivots at 16, scales excluded */
+    double stored_bits_per_entry; /* slot_bytes * 8 / (L * H * d_k * d_v): codes + scales + padding */
+    double compression_vs_fp32;   /* 32 / stored_bits_per_entry */
+} sq_plan_desc;
+
+/* ---- plan (CPU) --------------------------------------------------------
+ * Offline planner (hyper.ai summary, 方法, lifetime-aware bit allocation and
+ * the row-impact score): lifetime weight per unit from its mean log retention,
+ * reconstruction distortion at each candidate width on calibration snapshots,
+ * FP16 pivots for the riskiest units, an exact budgeted allocation of widths,
+ * and the packed layout.  Runs on the host only; the plan owns host memory.
+ * Errors: SQ_ERR_ARG / SQ_ERR_UNSUPPORTED on bad configuration. */
+sq_status sq_plan_create(const sq_plan_cfg* cfg, sq_plan** out);
+void      sq_plan_destroy(sq_plan* plan);
+sq_status sq_plan_describe(const sq_plan* plan, sq_plan_desc* out);
+/* Per-unit planner quantities (host arrays of n_units; any pointer may be NULL):
+ * mean log retention, lifetime weight, distortion [n_units][n_widths], width (16 = pivot). */
+sq_status sq_plan_units(const sq_plan* plan, double* lbar, double* lifetime, double* distortion,
+                        int32_t* unit_bits);
+/* Per-row tables in canonical row order (host arrays [L][H][d_k]; any may be NULL):
+ * quantization width (16 = pivot row) and the row-impact score used by the step. */
+sq_status sq_plan_rows(const sq_plan* plan, int32_t* row_bits, float* impact);
+/* Serialize to / restore from a byte buffer (host).  With buf == NULL, *bytes
+ * receives the size needed.  sq_plan_load validates the buffer. */
+sq_status sq_plan_save(const sq_plan* plan, void* buf, size_t* bytes);
+sq_status sq_plan_load(const void* buf, size_t bytes, sq_plan** out);
+/* The built-in calibration generator for one (layer, head): q, k [S][T][d_k]
+ * (unit L2 norm), v [S][T][d_v], beta [S][T] (host arrays, fp32). */
+sq_status sq_calib_generate(uint64_t seed, int32_t layer, int32_t head, int32_t n_seg,
+                            int32_t seg_len, int32_t d_k, int32_t d_v,
+                            float* q, float* k, float* v, float* beta);
+
+/* ---- pool (device) -----------------------------------------------------
+ * The caller owns the pool memory: n_slots slots of desc.slot_bytes each.  A
+ * request's state for (layer l, head h) lives in its slot at the plan's
+ * offset for (l, h).  Binding copies the plan's layout tables to the current
+ * device (the pool object owns those small allocations until destroyed). */
+sq_status sq_pool_bytes(const sq_plan* plan, int32_t n_slots, size_t* bytes);
+sq_status sq_pool_create(const sq_plan* plan, void* d_pool, size_t pool_bytes, int32_t n_slots,
+                         sq_pool** out);
+void      sq_pool_destroy(sq_pool* pool);
+
+#define SQ_STEP_SPLIT    1u       /* two kernels: readout on stream_main, fit + pack on stream_aux */
+#define SQ_STEP_VALIDATE 2u       /* copy the slot list to the host and check range and uniqueness */
+
+/* ---- state_step --------------------------------------------------------
+ * One decode step for batch requests over layers [layer0, layer0 + n_layers)
+ * and every head (rcap.io post, decode-step pseudocode; hyper.ai 方法):
+ *   S = unpack(codes, r, c, pivots);  X = D S + beta k (v^T - k^T D S);
+ *   y = X^T q (written to d_y before requantization);
+ *   r = binary16(sqrt(rowmax|X| / w));  c = argmin over the grid of the
+ *   impact-weighted reconstruction error;  codes = clamp(rint(X / (r c))).
+ * d_slots[b] is the pool slot of request b (int32, device).  d_q, d_k
+ * [n_layers][batch][H][d_k]; d_v, d_y [..][d_v]; d_beta [..]; d_gate is alpha
+ * in (0, 1]: [n_layers][batch][H] (GDN) or [n_layers][batch][H][d_k] (KDA).
+ * Slots must be distinct within a call (otherwise the result is undefined;
+ * SQ_STEP_VALIDATE checks it and returns SQ_ERR_SLOT).  Enqueued on
+ * stream_main (and stream_aux with SQ_STEP_SPLIT; ordered by events, the call
+ * returns with stream_main waiting for all of its work). */
+sq_status sq_state_step(sq_pool* pool, int32_t layer0, int32_t n_layers, int32_t batch,
+                        const int32_t* d_slots, const float* d_q, const float* d_k,
+                        const float* d_v, const float* d_gate, const float* d_beta, float* d_y,
+                        void* stream_main, void* stream_aux, uint32_t flags);
+
+/* ---- pack / unpack -----------------------------------------------------
+ * sq_pack quantizes float states d_X [n_layers][batch][H][d_k][d_v] into the
+ * slots (row factors, column fit, rounding; the requantization half of a
+ * step).  sq_unpack writes the dequantized states r_i c_j Q_ij (binary16
+ * value on pivot rows) to d_X in the same layout (rcap.io pseudocode, unpack). */
+sq_status sq_pack(sq_pool* pool, int32_t layer0, int32_t n_layers, int32_t batch,
+                  const int32_t* d_slots, const float* d_X, void* stream);
+sq_status sq_unpack(sq_pool* pool, int32_t layer0, int32_t n_layers, int32_t batch,
+                    const int32_t* d_slots, float* d_X, void* stream);
+
+/* ---- export / import ---------------------------------------------------
+ * Canonical (layout-independent) form of the packed states, in canonical
+ * key-row order: d_codes int16 [n_layers][batch][H][d_k][d_v] holds the
+ * signed code on code rows and the binary16 bit pattern on pivot rows;
+ * d_r uint16 [..][d_k] binary16 row factors (1.0 on pivot rows); d_c uint16
+ * [..][d_v] binary16 column scales.  Import clamps codes to each row's range. */
+sq_status sq_export(sq_pool* pool, int32_t layer0, int32_t n_layers, int32_t batch,
+                    const int32_t* d_slots, int16_t* d_codes, uint16_t* d_r, uint16_t* d_c,
+                    void* stream);
+sq_status sq_import(sq_pool* pool, int32_t layer0, int32_t n_layers, int32_t batch,
+                    const int32_t* d_slots, const int16_t* d_codes, const uint16_t* d_r,
+                    const uint16_t* d_c, void* stream);
+
+/* ---- comparators (same inputs, other state formats) --------------------
+ * Uniform INT8 per-row state (the baseline the pages compare against): state
+ * i = (layer * n_slots + slot) * H + head holds int8 codes [d_k][d_v] at
+ * d_codes + i*d_k*d_v and a binary32 row scale [d_k] at d_scales + i*d_k;
+ * step: S = s_i Q, the same update and readout, s_i = max_j |X_ij| / 127,
+ * Q = clamp(rint(X / s_i), +-127).  sq_fp32_step keeps float states d_S
+ * [(layer * n_slots + slot) * H + head][d_k][d_v] (no quantization). */
+sq_status sq_int8_step(int32_t form, int32_t n_heads, int32_t dim_k, int32_t dim_v, int32_t n_slots,
+                       int32_t layer0, int32_t n_layers, int32_t batch, const int32_t* d_slots,
+                       int8_t* d_codes, float* d_scales, const float* d_q, const float* d_k,
+                       const float* d_v, const float* d_gate, const float* d_beta, float* d_y,
+                       void* stream);
+sq_status sq_fp32_step(int32_t form, int32_t n_heads, int32_t dim_k, int32_t dim_v, int32_t n_slots,
+                       int32_t layer0, int32_t n_layers, int32_t batch, const int32_t* d_slots,
+                       float* d_S, const float* d_q, const float* d_k, const float* d_v,
+                       const float* d_gate, const float* d_beta, float* d_y, void* stream);
+/* Streaming copy of n_bytes (multiple of 16, 16-byte aligned) for measuring achievable HBM bandwidth. */
+sq_status sq_copy(const void* d_src, void* d_dst, size_t n_bytes, void* stream);
+
+/* ---- errors / info ------------------------------------------------------ */
+const char* sq_status_str(sq_status s);
+const char* sq_last_error(void);          /* thread-local; "" if none */
+/* Shapes (d_k, d_v) the step kernels are compiled for, as pairs: out[2i], out[2i+1]. */
+int32_t     sq_supported_shapes(int32_t* out, int32_t max_pairs);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STEPQ_H */

@@ -1,0 +1,99 @@
+"""ctypes declarations of libstepq.so (the C ABI in include/stepq.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from ctypes import POINTER, c_double, c_float, c_int16, c_int32, c_int8, c_size_t, c_uint16, c_uint32, c_uint64, c_void_p
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libstepq.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "stepq.h")
+
+SQ_OK = 0
+SQ_FORM_GDN, SQ_FORM_KDA = 0, 1
+SQ_UNIT_HEAD, SQ_UNIT_ROW = 0, 1
+SQ_STEP_SPLIT, SQ_STEP_VALIDATE = 1, 2
+SQ_PIVOT_BITS = 16
+SQ_MAX_WIDTHS, SQ_MAX_GRID = 4, 8
+
+
+class SqPlanCfg(ctypes.Structure):
+    _fields_ = [
+        ("form", c_int32), ("unit", c_int32),
+        ("n_layers", c_int32), ("n_heads", c_int32), ("d_k", c_int32), ("d_v", c_int32),
+        ("n_widths", c_int32), ("widths", c_int32 * SQ_MAX_WIDTHS),
+        ("budget_milli", c_int32), ("pivot_ppm", c_int32),
+        ("n_grid", c_int32), ("grid", c_float * SQ_MAX_GRID),
+        ("gate", POINTER(c_float)), ("impact", POINTER(c_float)), ("unit_bits", POINTER(c_int32)),
+        ("calib_q", POINTER(c_float)), ("calib_k", POINTER(c_float)),
+        ("calib_v", POINTER(c_float)), ("calib_beta", POINTER(c_float)),
+        ("calib_seed", c_uint64), ("calib_segments", c_int32), ("calib_len", c_int32),
+        ("n_threads", c_int32),
+    ]
+
+
+class SqPlanDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", c_int32), ("n_heads", c_int32), ("d_k", c_int32), ("d_v", c_int32),
+        ("form", c_int32), ("unit", c_int32), ("n_units", c_int32), ("n_pivot_units", c_int32),
+        ("n_grid", c_int32), ("n_widths", c_int32), ("widths", c_int32 * SQ_MAX_WIDTHS),
+        ("slot_bytes", c_uint64),
+        ("code_bits_per_entry", c_double), ("stored_bits_per_entry", c_double),
+        ("compression_vs_fp32", c_double),
+    ]
+
+
+_P = c_void_p
+_SIGS = {
+    "sq_plan_create": (c_int32, [POINTER(SqPlanCfg), POINTER(c_void_p)]),
+    "sq_plan_destroy": (None, [_P]),
+    "sq_plan_describe": (c_int32, [_P, POINTER(SqPlanDesc)]),
+    "sq_plan_units": (c_int32, [_P, POINTER(c_double), POINTER(c_double), POINTER(c_double), POINTER(c_int32)]),
+    "sq_plan_rows": (c_int32, [_P, POINTER(c_int32), POINTER(c_float)]),
+    "sq_plan_save": (c_int32, [_P, _P, POINTER(c_size_t)]),
+    "sq_plan_load": (c_int32, [_P, c_size_t, POINTER(c_void_p)]),
+    "sq_calib_generate": (c_int32, [c_uint64, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                    POINTER(c_float), POINTER(c_float), POINTER(c_float), POINTER(c_float)]),
+    "sq_pool_bytes": (c_int32, [_P, c_int32, POINTER(c_size_t)]),
+    "sq_pool_create": (c_int32, [_P, _P, c_size_t, c_int32, POINTER(c_void_p)]),
+    "sq_pool_destroy": (None, [_P]),
+    "sq_state_step": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_uint32]),
+    "sq_pack": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P]),
+    "sq_unpack": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P]),
+    "sq_export": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P]),
+    "sq_import": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P]),
+    "sq_int8_step": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                               _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "sq_fp32_step": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                               _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "sq_copy": (c_int32, [_P, _P, c_size_t, _P]),
+    "sq_status_str": (ctypes.c_char_p, [c_int32]),
+    "sq_last_error": (ctypes.c_char_p, []),
+    "sq_supported_shapes": (c_int32, [POINTER(c_int32), c_int32]),
+}
+
+_lib = None
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/stepq.h."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(sq_[a-z0-9_]+)\s*\(", txt)))
+
+
+def load():
+    """Load libstepq.so.  Raises if it has not been built: there is no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m quantized_delta_rule_02_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

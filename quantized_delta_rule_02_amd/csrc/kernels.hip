@@ -1,0 +1,890 @@
+// gfx950 kernels of the quantized gated-delta state step.
+//
+// One workgroup of NW wave64s processes one (request, layer, head) state.
+// Wave w owns RPW storage rows; lane l owns CPL adjacent value columns, so
+//   * every key-row quantity (gate, k, q, row factor, impact) is uniform across
+//     a wave and is read from LDS by broadcast,
+//   * the column reductions k^T D S, q^T D S, the column base and the fit
+//     objective accumulate in registers, then across the NW waves through LDS,
+//   * the row maximum is the one cross-lane reduction (transpose-reduce).
+// The state never leaves registers between the unpack and the pack: HBM sees
+// the packed codes and scales once in each direction plus q, k, v, gate, beta, y.
+// See internal.h for the record layout.
+//
+// Method (STEPQuant pages): rcap.io post, decode-step pseudocode (unpack ->
+// X = D S + beta k (v^T - k^T D S) -> y = X^T q before requantization -> row
+// factors sqrt(row magnitude / row impact) -> impact-weighted column fit ->
+// round at each unit's width); hyper.ai summary, section 方法 (Method), on the
+// fused reconstruction + update + readout kernel and the dual-axis fit and
+// packed write-back.  The column fit searches a fixed grid of candidates
+// gamma * c0 with c0 = max_i |X_ij| / (r_i qmax_i).
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+#include "launch.h"
+
+namespace sq {
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xFFFFu)));
+}
+__device__ __forceinline__ uint32_t f2h_bits(float x) {
+    return (uint32_t)__half_as_ushort(__float2half_rn(x));
+}
+// binary16 value (as float) of a positive scale clamped to [2^-14, 65504]
+__device__ __forceinline__ float scale_fp16(float x) {
+    x = fminf(fmaxf(x, 0x1p-14f), 65504.0f);
+    return __half2float(__float2half_rn(x));
+}
+__device__ __forceinline__ float med3(float x, float lo, float hi) {
+    return __builtin_amdgcn_fmed3f(x, lo, hi);
+}
+__device__ __forceinline__ int bias_of(int bits) { return bits == 16 ? 0 : (1 << (bits - 1)); }
+
+// 16 entries of one lane in one group <-> container dwords (internal.h)
+__device__ __forceinline__ void unpack4(const uint32_t* d, float* o) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int i = e & 7;
+        o[e] = (float)((d[e >> 3] >> (8 * (i & 3) + 4 * (i >> 2))) & 0xFu);
+    }
+}
+__device__ __forceinline__ void unpack6(const uint32_t* d, float* o) {
+#pragma unroll
+    for (int e = 0; e < 12; ++e) o[e] = (float)((d[e >> 2] >> (8 * (e & 3))) & 0x3Fu);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t s = 8 * k + 6;
+        o[12 + k] = (float)(((d[0] >> s) & 3u) | (((d[1] >> s) & 3u) << 2) | (((d[2] >> s) & 3u) << 4));
+    }
+}
+__device__ __forceinline__ void unpack8(const uint32_t* d, float* o) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = (float)((d[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+}
+__device__ __forceinline__ void pack4(const int* c, uint32_t* d) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x |= (uint32_t)(c[8 * w + i] & 0xF) << (8 * (i & 3) + 4 * (i >> 2));
+        d[w] = x;
+    }
+}
+__device__ __forceinline__ void pack6(const int* c, uint32_t* d) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t b = (uint32_t)(c[4 * w + k] & 0x3F) | ((((uint32_t)c[12 + k] >> (2 * w)) & 3u) << 6);
+            x |= b << (8 * k);
+        }
+        d[w] = x;
+    }
+}
+__device__ __forceinline__ void pack8(const int* c, uint32_t* d) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x |= (uint32_t)(c[4 * w + k] & 0xFF) << (8 * k);
+        d[w] = x;
+    }
+}
+
+template <int NDW>
+__device__ __forceinline__ void load_dw(const uint8_t* p, uint32_t* d) {
+    if constexpr (NDW == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        d[0] = v.x; d[1] = v.y;
+    } else if constexpr (NDW == 3) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+        d[0] = q[0]; d[1] = q[1]; d[2] = q[2];
+    } else if constexpr (NDW == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    } else {
+        const uint4 v0 = reinterpret_cast<const uint4*>(p)[0];
+        const uint4 v1 = reinterpret_cast<const uint4*>(p)[1];
+        d[0] = v0.x; d[1] = v0.y; d[2] = v0.z; d[3] = v0.w;
+        d[4] = v1.x; d[5] = v1.y; d[6] = v1.z; d[7] = v1.w;
+    }
+}
+template <int NDW>
+__device__ __forceinline__ void store_dw(uint8_t* p, const uint32_t* d) {
+    if constexpr (NDW == 2) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(d[0], d[1]);
+    } else if constexpr (NDW == 3) {
+        uint32_t* q = reinterpret_cast<uint32_t*>(p);
+        q[0] = d[0]; q[1] = d[1]; q[2] = d[2];
+    } else if constexpr (NDW == 4) {
+        *reinterpret_cast<uint4*>(p) = make_uint4(d[0], d[1], d[2], d[3]);
+    } else {
+        reinterpret_cast<uint4*>(p)[0] = make_uint4(d[0], d[1], d[2], d[3]);
+        reinterpret_cast<uint4*>(p)[1] = make_uint4(d[4], d[5], d[6], d[7]);
+    }
+}
+
+// Transpose-reduce of per-row maxima across the LPR lanes of a row band.
+// Before: v[0..N) = this lane's partial max of local rows 0..N-1.  After:
+// v[0] = the full max of local row `row` (the same row on LPR/N lanes).
+template <int D, int N>
+struct RowMax {
+    static __device__ __forceinline__ void run(float* v, int lane, int& row) {
+        if constexpr (D >= 1) {
+            if constexpr (N > 1) {
+                const bool hi = (lane & D) != 0;
+#pragma unroll
+                for (int i = 0; i < N / 2; ++i) {
+                    const float keep = hi ? v[i + N / 2] : v[i];
+                    const float send = hi ? v[i] : v[i + N / 2];
+                    v[i] = fmaxf(keep, __shfl_xor(send, D));
+                }
+                if (hi) row += N / 2;
+                RowMax<D / 2, N / 2>::run(v, lane, row);
+            } else {
+                v[0] = fmaxf(v[0], __shfl_xor(v[0], D));
+                RowMax<D / 2, 1>::run(v, lane, row);
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------- the step kernel
+
+template <int DK, int DV>
+struct Shape {
+    static constexpr int CPL = cpl_of(DV);
+    static constexpr int LPR = lpr_of(DV);
+    static constexpr int GR = gr_of(DV);
+    static constexpr int RPW = rpw_of(DK, DV);
+    static constexpr int NW = nw_of(DK, DV);
+    static constexpr int GPW = RPW / GR;
+    static constexpr int EPL = RPW * CPL;
+    static constexpr int NG = ng_of(DK, DV);
+    static_assert(RPW <= LPR, "row band taller than the lanes that reduce it");
+    static_assert(GPW * GR == RPW && EPL == 16 * GPW, "group tiling");
+};
+
+template <int DK, int DV>
+struct StepSmem {
+    float A[DK], nb[DK], ck[DK], cq[DK], pk[DK], pq[DK], al[DK], bk[DK];
+    float rn[DK], ir[DK], sw[DK], iq[DK], qm[DK], w[DK];
+    int rb[DK];
+    float part[Shape<DK, DV>::NW][4][DV];
+    float red[Shape<DK, DV>::NW][4];
+};
+
+template <int DK, int DV, int MODE>
+__global__ void __launch_bounds__(nw_of(DK, DV) * 64)
+k_state(StepParams a) {
+    using Sh = Shape<DK, DV>;
+    constexpr int CPL = Sh::CPL, LPR = Sh::LPR, GR = Sh::GR, RPW = Sh::RPW, NW = Sh::NW;
+    constexpr int GPW = Sh::GPW, EPL = Sh::EPL, NG = Sh::NG;
+    __shared__ StepSmem<DK, DV> sm;
+
+    const int sid = blockIdx.x + a.state0;
+    const int h = sid % a.n_heads;
+    const int b = (sid / a.n_heads) % a.batch;
+    const int l = a.layer0 + sid / (a.n_heads * a.batch);
+    const int lh = l * a.n_heads + h;
+    const int slot = a.slots[b];
+    uint8_t* rec = a.pool + (uint64_t)slot * a.slot_bytes + a.t.rec_off[lh];
+    uint16_t* rs = reinterpret_cast<uint16_t*>(rec + a.t.scale_off[lh]);   // row factors, then column scales
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const bool act = lane < LPR;
+    const int col0 = lane * CPL;
+    const uint8_t* gbits = a.t.grp_bits + (size_t)lh * NG;
+    const uint32_t* goff = a.t.grp_off + (size_t)lh * NG;
+    const uint8_t hflags = a.t.head_flags[lh];
+
+    // ---- phase 0: per-row coefficients (one thread per storage row)
+    constexpr bool kNeedOld = (MODE != kModePack);
+    constexpr bool kUpdate = (MODE == kModeStep || MODE == kModeSplitA || MODE == kModeSplitB);
+    float kq_part = 0.f, kb_part = 0.f, qb_part = 0.f;
+    if (tid < DK) {
+        const int t = tid;
+        const int rbits = a.t.row_bits[(size_t)lh * DK + t];
+        const int sb = gbits[t / GR];
+        const bool piv = rbits == 16;
+        sm.rb[t] = rbits;
+        sm.w[t] = a.t.row_w[(size_t)lh * DK + t];
+        if constexpr (kNeedOld) {
+            const float rold = h2f(rs[t]);
+            float al = 1.f, kk = 0.f, qq = 0.f, bt = 0.f;
+            if constexpr (kUpdate) {
+                const int i = a.t.perm[(size_t)lh * DK + t];
+                kk = a.k[(size_t)sid * DK + i];
+                qq = a.q[(size_t)sid * DK + i];
+                al = (a.form == 1) ? a.gate[(size_t)sid * DK + i] : a.gate[sid];
+                bt = a.beta[sid];
+            }
+            const float A = piv ? 0.f : al * rold;
+            const float bias = (float)bias_of(sb);
+            sm.A[t] = A;
+            sm.nb[t] = -A * bias;
+            sm.ck[t] = A * kk;
+            sm.cq[t] = A * qq;
+            sm.pk[t] = piv ? al * kk : 0.f;
+            sm.pq[t] = piv ? al * qq : 0.f;
+            sm.al[t] = piv ? al : 0.f;
+            sm.bk[t] = bt * kk;
+            kq_part = kk * qq;
+            kb_part = A * kk * bias;
+            qb_part = A * qq * bias;
+        }
+    }
+    if constexpr (kUpdate) {
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            kq_part += __shfl_xor(kq_part, d);
+            kb_part += __shfl_xor(kb_part, d);
+            qb_part += __shfl_xor(qb_part, d);
+        }
+        if (lane == 0) {
+            sm.red[wave][0] = kq_part;
+            sm.red[wave][1] = kb_part;
+            sm.red[wave][2] = qb_part;
+        }
+    }
+    __syncthreads();
+
+    float X[EPL];
+    float c_old[CPL];
+    if constexpr (kNeedOld) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) c_old[c] = act ? h2f(rs[DK + col0 + c]) : 1.f;
+    }
+
+    // ---- phase 1: load + unpack (biased codes / pivot values), column accumulations
+    if constexpr (MODE == kModePack) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int t = wave * RPW + e / CPL;
+            const int i = a.t.perm[(size_t)lh * DK + t];
+            X[e] = act ? a.x_in[((size_t)sid * DK + i) * DV + col0 + (e % CPL)] : 0.f;
+        }
+    } else {
+        float U1[CPL], P1[CPL], U2[CPL], P2[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) U1[c] = P1[c] = U2[c] = P2[c] = 0.f;
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) {
+            const int gg = wave * GPW + g;
+            const int sb = gbits[gg];
+            const uint8_t* gp = rec + goff[gg];
+            float* xg = &X[16 * g];
+            uint32_t d[8];
+            if (sb == 4) {
+                if (act) load_dw<2>(gp + lane * 8, d); else d[0] = d[1] = 0;
+                unpack4(d, xg);
+            } else if (sb == 6) {
+                if (act) load_dw<3>(gp + lane * 12, d); else d[0] = d[1] = d[2] = 0;
+                unpack6(d, xg);
+            } else if (sb == 8) {
+                if (act) load_dw<4>(gp + lane * 16, d); else d[0] = d[1] = d[2] = d[3] = 0;
+                unpack8(d, xg);
+            } else {
+                if (act) load_dw<8>(gp + lane * 32, d);
+                else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) d[i] = 0;
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = wave * RPW + 16 * g / CPL + e / CPL;
+                    const uint32_t bits = (d[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    xg[e] = (sm.rb[t] == 16) ? h2f(bits) : (float)(int16_t)bits;
+                }
+            }
+            if constexpr (MODE == kModeStep || MODE == kModeSplitA) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = wave * RPW + (16 * g + e) / CPL;
+                    const int c = e % CPL;
+                    U1[c] = fmaf(sm.ck[t], xg[e], U1[c]);
+                    P1[c] = fmaf(sm.cq[t], xg[e], P1[c]);
+                }
+                if (sb == 16) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int t = wave * RPW + (16 * g + e) / CPL;
+                        const int c = e % CPL;
+                        U2[c] = fmaf(sm.pk[t], xg[e], U2[c]);
+                        P2[c] = fmaf(sm.pq[t], xg[e], P2[c]);
+                    }
+                }
+            }
+        }
+
+        if constexpr (MODE == kModeUnpack) {
+            // dequantized state r_i c_j Q_ij (binary16 value on pivot rows) -> canonical float layout
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const int t = wave * RPW + e / CPL;
+                const int c = e % CPL;
+                const bool piv = sm.rb[t] == 16;
+                const float s = piv ? X[e] : c_old[c] * fmaf(sm.A[t], X[e], sm.nb[t]);
+                const int i = a.t.perm[(size_t)lh * DK + t];
+                if (act) a.x_out[((size_t)sid * DK + i) * DV + col0 + c] = s;
+            }
+            return;
+        }
+
+        float ecol[CPL];
+        if constexpr (MODE == kModeStep || MODE == kModeSplitA) {
+            if (act) {
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    sm.part[wave][0][col0 + c] = U1[c];
+                    sm.part[wave][1][col0 + c] = P1[c];
+                    sm.part[wave][2][col0 + c] = U2[c];
+                    sm.part[wave][3][col0 + c] = P2[c];
+                }
+            }
+            __syncthreads();
+            float kq = 0.f, kb = 0.f, qb = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                kq += sm.red[w][0];
+                kb += sm.red[w][1];
+                qb += sm.red[w][2];
+            }
+            const float bt = a.beta[sid];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                float su = 0.f, sp = 0.f, su2 = 0.f, sp2 = 0.f;
+                if (act) {
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        su += sm.part[w][0][col0 + c];
+                        sp += sm.part[w][1][col0 + c];
+                        su2 += sm.part[w][2][col0 + c];
+                        sp2 += sm.part[w][3][col0 + c];
+                    }
+                }
+                const float u = fmaf(c_old[c], su - kb, su2);      // k^T D S
+                const float p = fmaf(c_old[c], sp - qb, sp2);      // q^T D S
+                const float e = act ? a.v[(size_t)sid * DV + col0 + c] - u : 0.f;
+                ecol[c] = e;
+                if (act && wave == 0) a.y[(size_t)sid * DV + col0 + c] = fmaf(bt * kq, e, p);
+                if constexpr (MODE == kModeSplitA) {
+                    if (act && wave == 0) a.e_buf[(size_t)sid * DV + col0 + c] = e;
+                }
+            }
+            if constexpr (MODE == kModeSplitA) return;
+        } else {
+            // split arrangement, second half: e = v - k^T D S comes from the first kernel
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) ecol[c] = act ? a.e_buf[(size_t)sid * DV + col0 + c] : 0.f;
+        }
+
+        // ---- phase 2: the updated float state X = D S + beta k e^T in registers
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) {
+            const int sb = gbits[wave * GPW + g];
+            if (sb != 16) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = wave * RPW + (16 * g + e) / CPL;
+                    const int c = e % CPL;
+                    X[16 * g + e] = fmaf(c_old[c], fmaf(sm.A[t], X[16 * g + e], sm.nb[t]), sm.bk[t] * ecol[c]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = wave * RPW + (16 * g + e) / CPL;
+                    const int c = e % CPL;
+                    const bool piv = sm.rb[t] == 16;
+                    const float dq = piv ? sm.al[t] * X[16 * g + e] : c_old[c] * (sm.A[t] * X[16 * g + e]);
+                    X[16 * g + e] = fmaf(sm.bk[t], ecol[c], dq);
+                }
+            }
+        }
+    }
+
+    // ---- phase 3: row factors r_i = binary16(sqrt(max_j |X_ij| / w_i)) (rows are wave-uniform)
+    {
+        float rm[RPW];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            float m = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) m = fmaxf(m, fabsf(X[r * CPL + c]));
+            rm[r] = act ? m : 0.f;
+        }
+        int row = 0;
+        RowMax<LPR / 2, RPW>::run(rm, lane, row);
+        if (act && (lane & (LPR / RPW - 1)) == 0) {
+            const int t = wave * RPW + row;
+            const int rbits = sm.rb[t];
+            const bool piv = rbits == 16;
+            const float m = rm[0];
+            const float w = sm.w[t];
+            float rn = 1.f;
+            if (!piv && m > 0.f) rn = scale_fp16(sqrtf(m / w));
+            const float qmax = piv ? 0.f : (float)((1 << (rbits - 1)) - 1);
+            sm.rn[t] = rn;
+            sm.ir[t] = 1.f / rn;
+            sm.sw[t] = piv ? 0.f : sqrtf(w) * rn;
+            sm.iq[t] = piv ? 0.f : 1.f / qmax;
+            sm.qm[t] = qmax;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 4: t = X / r_i (code rows; pivot rows have r = 1) and the column base
+    float c0[CPL];
+    {
+        float c0p[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) c0p[c] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int t = wave * RPW + e / CPL;
+            const int c = e % CPL;
+            X[e] = X[e] * sm.ir[t];
+            c0p[c] = fmaxf(c0p[c], fabsf(X[e]) * sm.iq[t]);
+        }
+        if (act) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) sm.part[wave][0][col0 + c] = c0p[c];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            float m = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) m = fmaxf(m, act ? sm.part[w][0][col0 + c] : 0.f);
+            c0[c] = m;
+        }
+        __syncthreads();   // part[] is reused below
+    }
+
+    // ---- phase 5: column fit over the candidate grid, up to four candidates per LDS round
+    float cbest[CPL], fbest[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        cbest[c] = 1.f;
+        fbest[c] = __builtin_inff();
+    }
+    if (hflags & kHasCodeRows) {
+        for (int g0 = 0; g0 < a.n_grid; g0 += 4) {
+            const int ng = min(4, a.n_grid - g0);
+            float cg[4][CPL], icg[4][CPL], Fp[4][CPL];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const float gam = (j < ng) ? a.grid[g0 + j] : 1.f;
+                    cg[j][c] = scale_fp16(gam * c0[c]);
+                    icg[j][c] = 1.f / cg[j][c];
+                    Fp[j][c] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const int t = wave * RPW + e / CPL;
+                const int c = e % CPL;
+                const float qm = sm.qm[t], sw = sm.sw[t];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (j < ng) {
+                        const float Qc = med3(rintf(X[e] * icg[j][c]), -qm, qm);
+                        const float dd = sw * fmaf(X[e], icg[j][c], -Qc);
+                        Fp[j][c] = fmaf(dd, dd, Fp[j][c]);
+                    }
+                }
+            }
+            if (act) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) sm.part[wave][j][col0 + c] = Fp[j][c];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j < ng) {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        float F = 0.f;
+#pragma unroll
+                        for (int w = 0; w < NW; ++w) F += act ? sm.part[w][j][col0 + c] : 0.f;
+                        F *= cg[j][c] * cg[j][c];
+                        if (F < fbest[c]) {
+                            fbest[c] = F;
+                            cbest[c] = cg[j][c];
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    float ic[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        if (!(c0[c] > 0.f)) cbest[c] = 1.f;      // all-zero column: scale 1, zero codes
+        ic[c] = 1.f / cbest[c];
+    }
+
+    // ---- phase 6: round, pack and write back codes, row factors and column scales
+#pragma unroll
+    for (int g = 0; g < GPW; ++g) {
+        const int gg = wave * GPW + g;
+        const int sb = gbits[gg];
+        uint8_t* gp = rec + goff[gg];
+        int code[16];
+        uint32_t d[8];
+        if (sb != 16) {
+            const int bias = bias_of(sb);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = wave * RPW + (16 * g + e) / CPL;
+                const int c = e % CPL;
+                const float qm = sm.qm[t];
+                code[e] = (int)med3(rintf(X[16 * g + e] * ic[c]), -qm, qm) + bias;
+            }
+            if (act) {
+                if (sb == 4) { pack4(code, d); store_dw<2>(gp + lane * 8, d); }
+                else if (sb == 6) { pack6(code, d); store_dw<3>(gp + lane * 12, d); }
+                else { pack8(code, d); store_dw<4>(gp + lane * 16, d); }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int t = wave * RPW + (16 * g + e) / CPL;
+                const int c = e % CPL;
+                const float qm = sm.qm[t];
+                const bool piv = sm.rb[t] == 16;
+                const uint32_t bits = piv ? f2h_bits(fminf(fmaxf(X[16 * g + e], -65504.f), 65504.f))
+                                          : ((uint32_t)(int)med3(rintf(X[16 * g + e] * ic[c]), -qm, qm) & 0xFFFFu);
+                code[e] = (int)bits;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) d[i] = (uint32_t)code[2 * i] | ((uint32_t)code[2 * i + 1] << 16);
+            if (act) store_dw<8>(gp + lane * 32, d);
+        }
+    }
+    if (tid < DK) rs[tid] = (uint16_t)f2h_bits(sm.rn[tid]);
+    if (wave == 0 && act) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) rs[DK + col0 + c] = (uint16_t)f2h_bits(cbest[c]);
+    }
+}
+
+// ---------------------------------------------------------------- export / import
+
+template <int DK, int DV, bool EXPORT>
+__global__ void __launch_bounds__(nw_of(DK, DV) * 64)
+k_codec(CodecParams a) {
+    using Sh = Shape<DK, DV>;
+    constexpr int CPL = Sh::CPL, LPR = Sh::LPR, RPW = Sh::RPW, GPW = Sh::GPW, NG = Sh::NG;
+    const int sid = blockIdx.x;
+    const int h = sid % a.n_heads;
+    const int b = (sid / a.n_heads) % a.batch;
+    const int l = a.layer0 + sid / (a.n_heads * a.batch);
+    const int lh = l * a.n_heads + h;
+    uint8_t* rec = a.pool + (uint64_t)a.slots[b] * a.slot_bytes + a.t.rec_off[lh];
+    uint16_t* rs = reinterpret_cast<uint16_t*>(rec + a.t.scale_off[lh]);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col0 = lane * CPL;
+    const uint16_t* perm = a.t.perm + (size_t)lh * DK;
+    const uint8_t* rbits = a.t.row_bits + (size_t)lh * DK;
+    if (lane < LPR) {
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) {
+            const int gg = wave * GPW + g;
+            const int sb = a.t.grp_bits[(size_t)lh * NG + gg];
+            uint8_t* gp = rec + a.t.grp_off[(size_t)lh * NG + gg];
+            const int bias = bias_of(sb);
+            int code[16];
+            uint32_t d[8];
+            if constexpr (EXPORT) {
+                if (sb == 16) {
+                    load_dw<8>(gp + lane * 32, d);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) code[e] = (int)((d[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                } else {
+                    float f[16];
+                    if (sb == 4) { load_dw<2>(gp + lane * 8, d); unpack4(d, f); }
+                    else if (sb == 6) { load_dw<3>(gp + lane * 12, d); unpack6(d, f); }
+                    else { load_dw<4>(gp + lane * 16, d); unpack8(d, f); }
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) code[e] = (int)f[e] - bias;
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = wave * RPW + (16 * g + e) / CPL;
+                    const int i = perm[t];
+                    a.codes[((size_t)sid * DK + i) * DV + col0 + e % CPL] = (int16_t)code[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int t = wave * RPW + (16 * g + e) / CPL;
+                    const int i = perm[t];
+                    int v = a.codes[((size_t)sid * DK + i) * DV + col0 + e % CPL];
+                    const int rb = rbits[t];
+                    if (rb == 16) {
+                        code[e] = v & 0xFFFF;
+                    } else {
+                        const int qm = (1 << (rb - 1)) - 1;
+                        v = v < -qm ? -qm : (v > qm ? qm : v);
+                        code[e] = (sb == 16) ? (v & 0xFFFF) : v + bias;
+                    }
+                }
+                if (sb == 4) { pack4(code, d); store_dw<2>(gp + lane * 8, d); }
+                else if (sb == 6) { pack6(code, d); store_dw<3>(gp + lane * 12, d); }
+                else if (sb == 8) { pack8(code, d); store_dw<4>(gp + lane * 16, d); }
+                else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) d[i] = (uint32_t)code[2 * i] | ((uint32_t)code[2 * i + 1] << 16);
+                    store_dw<8>(gp + lane * 32, d);
+                }
+            }
+        }
+    }
+    if (tid < DK) {
+        const int i = perm[tid];
+        if constexpr (EXPORT) a.r[(size_t)sid * DK + i] = rs[tid];
+        else rs[tid] = a.r[(size_t)sid * DK + i];
+    }
+    for (int j = tid; j < DV; j += blockDim.x) {
+        if constexpr (EXPORT) a.c[(size_t)sid * DV + j] = rs[DK + j];
+        else rs[DK + j] = a.c[(size_t)sid * DV + j];
+    }
+}
+
+// ---------------------------------------------------------------- comparators
+
+struct CmpParams {
+    int32_t n_heads, n_slots, layer0, batch, form;
+    const int32_t* slots;
+    int8_t* codes;
+    float* scales;
+    float* S;
+    const float *q, *k, *v, *gate, *beta;
+    float* y;
+};
+
+// Uniform INT8 per-row state and the unquantized FP32 state: same wave/lane
+// mapping as the packed step, row-major state storage.
+template <int DK, int DV, bool INT8>
+__global__ void __launch_bounds__(nw_of(DK, DV) * 64)
+k_cmp(CmpParams a) {
+    using Sh = Shape<DK, DV>;
+    constexpr int CPL = Sh::CPL, LPR = Sh::LPR, RPW = Sh::RPW, NW = Sh::NW, EPL = Sh::EPL;
+    __shared__ float s_ck[DK], s_cq[DK], s_al[DK], s_bk[DK], s_sc[DK];
+    __shared__ float s_part[NW][2][DV];
+    __shared__ float s_red[NW];
+    const int sid = blockIdx.x;
+    const int h = sid % a.n_heads;
+    const int b = (sid / a.n_heads) % a.batch;
+    const int ll = sid / (a.n_heads * a.batch);
+    const size_t st = ((size_t)(a.layer0 + ll) * a.n_slots + a.slots[b]) * a.n_heads + h;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const bool act = lane < LPR;
+    const int col0 = lane * CPL;
+    float kq = 0.f;
+    if (tid < DK) {
+        const float kk = a.k[(size_t)sid * DK + tid], qq = a.q[(size_t)sid * DK + tid];
+        const float al = (a.form == 1) ? a.gate[(size_t)sid * DK + tid] : a.gate[sid];
+        const float sc = INT8 ? a.scales[st * DK + tid] : 1.f;
+        s_ck[tid] = al * sc * kk;
+        s_cq[tid] = al * sc * qq;
+        s_al[tid] = al * sc;
+        s_bk[tid] = a.beta[sid] * kk;
+        kq = kk * qq;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) kq += __shfl_xor(kq, d);
+    if (lane == 0) s_red[wave] = kq;
+    __syncthreads();
+    float X[EPL];
+    float U[CPL], P[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) U[c] = P[c] = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const int t = wave * RPW + r;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            float x = 0.f;
+            if (act) {
+                if constexpr (INT8) x = (float)a.codes[(st * DK + t) * DV + col0 + c];
+                else x = a.S[(st * DK + t) * DV + col0 + c];
+            }
+            X[r * CPL + c] = x;
+            U[c] = fmaf(s_ck[t], x, U[c]);
+            P[c] = fmaf(s_cq[t], x, P[c]);
+        }
+    }
+    if (act) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            s_part[wave][0][col0 + c] = U[c];
+            s_part[wave][1][col0 + c] = P[c];
+        }
+    }
+    __syncthreads();
+    float kqs = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) kqs += s_red[w];
+    float ecol[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        float su = 0.f, sp = 0.f;
+        if (act) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                su += s_part[w][0][col0 + c];
+                sp += s_part[w][1][col0 + c];
+            }
+        }
+        const float e = act ? a.v[(size_t)sid * DV + col0 + c] - su : 0.f;
+        ecol[c] = e;
+        if (act && wave == 0) a.y[(size_t)sid * DV + col0 + c] = fmaf(a.beta[sid] * kqs, e, sp);
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const int t = wave * RPW + r;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) X[r * CPL + c] = fmaf(s_al[t], X[r * CPL + c], s_bk[t] * ecol[c]);
+    }
+    if constexpr (!INT8) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const int t = wave * RPW + r;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                if (act) a.S[(st * DK + t) * DV + col0 + c] = X[r * CPL + c];
+        }
+        return;
+    } else {
+        float rm[RPW];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            float m = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) m = fmaxf(m, fabsf(X[r * CPL + c]));
+            rm[r] = act ? m : 0.f;
+        }
+        int row = 0;
+        RowMax<LPR / 2, RPW>::run(rm, lane, row);
+        if (act && (lane & (LPR / RPW - 1)) == 0) {
+            const int t = wave * RPW + row;
+            const float s = rm[0] > 0.f ? rm[0] / 127.f : 1.f;
+            s_sc[t] = s;
+            a.scales[st * DK + t] = s;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const int t = wave * RPW + r;
+            const float inv = 1.f / s_sc[t];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const float qv = med3(rintf(X[r * CPL + c] * inv), -127.f, 127.f);
+                if (act) a.codes[(st * DK + t) * DV + col0 + c] = (int8_t)(int)qv;
+            }
+        }
+    }
+}
+
+__global__ void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int DK, int DV>
+static hipError_t launch_state_t(int mode, const StepParams& p, int n_states, hipStream_t s) {
+    const dim3 blk(Shape<DK, DV>::NW * 64);
+    switch (mode) {
+        case kModeStep: k_state<DK, DV, kModeStep><<<n_states, blk, 0, s>>>(p); break;
+        case kModePack: k_state<DK, DV, kModePack><<<n_states, blk, 0, s>>>(p); break;
+        case kModeUnpack: k_state<DK, DV, kModeUnpack><<<n_states, blk, 0, s>>>(p); break;
+        case kModeSplitA: k_state<DK, DV, kModeSplitA><<<n_states, blk, 0, s>>>(p); break;
+        case kModeSplitB: k_state<DK, DV, kModeSplitB><<<n_states, blk, 0, s>>>(p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+#define SQ_SHAPES(X) X(16, 16) X(64, 64) X(128, 128) X(128, 256)
+
+bool shape_compiled(int dk, int dv) {
+#define SQ_CASE(a, b) if (dk == a && dv == b) return true;
+    SQ_SHAPES(SQ_CASE)
+#undef SQ_CASE
+    return false;
+}
+
+int compiled_shapes(int32_t* out, int max_pairs) {
+    int n = 0;
+#define SQ_CASE(a, b) if (n < max_pairs && out) { out[2 * n] = a; out[2 * n + 1] = b; } ++n;
+    SQ_SHAPES(SQ_CASE)
+#undef SQ_CASE
+    return n;
+}
+
+hipError_t launch_state(int dk, int dv, int mode, const StepParams& p, int n_states, hipStream_t s) {
+    if (n_states <= 0) return hipSuccess;
+#define SQ_CASE(a, b) if (dk == a && dv == b) return launch_state_t<a, b>(mode, p, n_states, s);
+    SQ_SHAPES(SQ_CASE)
+#undef SQ_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_codec(int dk, int dv, bool do_export, const CodecParams& p, int n_states, hipStream_t s) {
+    if (n_states <= 0) return hipSuccess;
+#define SQ_CASE(a, b)                                                                                  \
+    if (dk == a && dv == b) {                                                                          \
+        const dim3 blk(Shape<a, b>::NW * 64);                                                          \
+        if (do_export) k_codec<a, b, true><<<n_states, blk, 0, s>>>(p);                               \
+        else k_codec<a, b, false><<<n_states, blk, 0, s>>>(p);                                        \
+        return hipGetLastError();                                                                      \
+    }
+    SQ_SHAPES(SQ_CASE)
+#undef SQ_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_cmp(int dk, int dv, bool int8, int form, int n_heads, int n_slots, int layer0, int n_layers,
+                      int batch, const int32_t* slots, int8_t* codes, float* scales, float* S, const float* q,
+                      const float* k, const float* v, const float* gate, const float* beta, float* y,
+                      hipStream_t s) {
+    CmpParams p{n_heads, n_slots, layer0, batch, form, slots, codes, scales, S, q, k, v, gate, beta, y};
+    const int n_states = n_layers * batch * n_heads;
+    if (n_states <= 0) return hipSuccess;
+#define SQ_CASE(a, b)                                                                                  \
+    if (dk == a && dv == b) {                                                                          \
+        const dim3 blk(Shape<a, b>::NW * 64);                                                          \
+        if (int8) k_cmp<a, b, true><<<n_states, blk, 0, s>>>(p);                                      \
+        else k_cmp<a, b, false><<<n_states, blk, 0, s>>>(p);                                          \
+        return hipGetLastError();                                                                      \
+    }
+    SQ_SHAPES(SQ_CASE)
+#undef SQ_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_copy(const void* src, void* dst, size_t n_bytes, hipStream_t s) {
+    const size_t n = n_bytes / 16;
+    if (n == 0) return hipSuccess;
+    const int threads = 256;
+    size_t blocks = (n + threads - 1) / threads;
+    if (blocks > 256 * 32) blocks = 256 * 32;
+    k_copy<<<dim3((unsigned)blocks), dim3(threads), 0, s>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst), n);
+    return hipGetLastError();
+}
+
+}  // namespace sq

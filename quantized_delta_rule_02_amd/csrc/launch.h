@@ -1,0 +1,21 @@
+// Kernel launchers (kernels.hip) called by the C ABI (api.cpp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace sq {
+
+bool shape_compiled(int dk, int dv);
+int compiled_shapes(int32_t* out, int max_pairs);
+hipError_t launch_state(int dk, int dv, int mode, const StepParams& p, int n_states, hipStream_t s);
+hipError_t launch_codec(int dk, int dv, bool do_export, const CodecParams& p, int n_states, hipStream_t s);
+hipError_t launch_cmp(int dk, int dv, bool int8, int form, int n_heads, int n_slots, int layer0, int n_layers,
+                      int batch, const int32_t* slots, int8_t* codes, float* scales, float* S, const float* q,
+                      const float* k, const float* v, const float* gate, const float* beta, float* y,
+                      hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, size_t n_bytes, hipStream_t s);
+
+}  // namespace sq

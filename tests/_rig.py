@@ -1,0 +1,143 @@
+"""GPU test rig: a plan + pool for (a slice of) a workload, driven through the C ABI binding.
+
+The plan's allocation comes from the oracle planner (passed to the library as a
+fixed per-unit allocation), so both sides quantize with identical widths and
+pivots.  Initial states come from the oracle (float64 warm-up, then the
+oracle's quantizer) and enter the pool through sq_import.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import quantized_delta_rule_02_amd as sq
+from oracle import planner as oplanner
+from oracle import quant
+from oracle.recurrence import run_unquantized
+from workloads import gen
+from workloads.configs import GDN, UNIT_HEAD, Workload
+
+from _parity import from_canonical, to_canonical
+
+
+def oracle_unit_bits(wl: Workload, n_layers: int, calib_segments=2, calib_len=32):
+    """Oracle planner on the first n_layers layers with a short calibration."""
+    gates = gen.unit_gates(wl)[:n_layers]
+    imp = gen.impact_scores(wl)[:n_layers]
+    seed = gen.calib_seed(wl)
+
+    def traces(l, h):
+        return gen.calib_traces(seed, l, h, calib_segments, calib_len, wl.d_k, wl.d_v)
+
+    p = oplanner.make_plan(wl.form, wl.unit, n_layers, wl.n_heads, wl.d_k, wl.d_v, wl.widths, wl.budget_milli,
+                           wl.pivot_ppm, wl.grid, gates, traces, impact=imp)
+    return p
+
+
+class Rig:
+    def __init__(self, wl: Workload, n_layers: int, batch: int, unit_bits=None, n_slots=None, slots=None,
+                 oplan=None):
+        import torch
+        self.torch = torch
+        self.wl = wl
+        self.nL, self.B, self.H, self.dk, self.dv = n_layers, batch, wl.n_heads, wl.d_k, wl.d_v
+        self.gates = gen.unit_gates(wl)[:n_layers]
+        self.impact = gen.impact_scores(wl)[:n_layers]
+        if unit_bits is None:
+            if oplan is None:
+                oplan = oracle_unit_bits(wl, n_layers)
+            unit_bits = oplan.unit_bits
+        self.unit_bits = np.asarray(unit_bits, np.int32)
+        self.plan = sq.sq_plan_create(
+            form=0 if wl.form == GDN else 1, unit=0 if wl.unit == UNIT_HEAD else 1, n_layers=n_layers,
+            n_heads=wl.n_heads, d_k=wl.d_k, d_v=wl.d_v, widths=wl.widths, budget_milli=wl.budget_milli,
+            pivot_ppm=wl.pivot_ppm, grid=wl.grid, gate=self.gates, impact=self.impact, unit_bits=self.unit_bits)
+        row_bits, w = sq.sq_plan_rows(self.plan)
+        self.row_bits = row_bits
+        self.n_slots = n_slots if n_slots is not None else batch
+        nbytes = sq.sq_pool_bytes(self.plan, self.n_slots)
+        self.mem = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        self.pool = sq.sq_pool_create(self.plan, self.mem, self.n_slots)
+        if slots is None:
+            slots = np.arange(batch, dtype=np.int32)
+        self.slots_np = np.asarray(slots, np.int32)
+        self.slots = torch.tensor(self.slots_np, dtype=torch.int32, device="cuda")
+        # oracle row plan per state, states in [layer][batch][head] order
+        N = n_layers * batch * wl.n_heads
+        bits = np.broadcast_to(row_bits[:, None], (n_layers, batch, wl.n_heads, wl.d_k)).reshape(N, wl.d_k)
+        ww = np.broadcast_to(w[:, None], (n_layers, batch, wl.n_heads, wl.d_k)).reshape(N, wl.d_k)
+        self.rows = quant.RowPlan(bits=np.where(bits == 16, 16, bits), pivot=bits == 16,
+                                  w=ww.astype(np.float64))
+        self.N = N
+
+    # ---- host <-> device
+    def _t(self, a, dtype=None):
+        t = self.torch.tensor(np.ascontiguousarray(a), device="cuda")
+        return t if dtype is None else t.to(dtype)
+
+    def alpha_states(self):
+        """Gate per state for the oracle: [N] (GDN) or [N, d_k] (KDA)."""
+        if self.wl.form == GDN:
+            return np.broadcast_to(self.gates[:, None, :], (self.nL, self.B, self.H)).reshape(-1).astype(np.float64)
+        return np.broadcast_to(self.gates[:, None], (self.nL, self.B, self.H, self.dk)).reshape(
+            -1, self.dk).astype(np.float64)
+
+    def gate_step(self):
+        """Gate array for one step in the library's layout."""
+        a = self.alpha_states().astype(np.float32)
+        return self._t(a.reshape(-1))
+
+    def import_packed(self, P: quant.Packed):
+        codes, r, c = to_canonical(P, self.rows)
+        sq.sq_import(self.pool, 0, self.nL, self.B, self.slots, self._t(codes), self._t(r), self._t(c))
+
+    def export_packed(self) -> quant.Packed:
+        torch = self.torch
+        codes = torch.zeros(self.N * self.dk * self.dv, dtype=torch.int16, device="cuda")
+        r = torch.zeros(self.N * self.dk, dtype=torch.int16, device="cuda")
+        c = torch.zeros(self.N * self.dv, dtype=torch.int16, device="cuda")
+        sq.sq_export(self.pool, 0, self.nL, self.B, self.slots, codes, r, c)
+        torch.cuda.synchronize()
+        return from_canonical(codes.cpu().numpy().reshape(self.N, self.dk, self.dv),
+                              r.cpu().numpy().reshape(self.N, self.dk), c.cpu().numpy().reshape(self.N, self.dv),
+                              self.rows)
+
+    def step(self, q, k, v, beta, flags=0, stream_aux=None):
+        """One library step; inputs are per-step arrays with N leading states.  Returns y [N, d_v]."""
+        torch = self.torch
+        y = torch.zeros(self.N * self.dv, dtype=torch.float32, device="cuda")
+        sq.sq_state_step(self.pool, 0, self.nL, self.B, self.slots, self._t(q.reshape(-1), torch.float32),
+                         self._t(k.reshape(-1), torch.float32), self._t(v.reshape(-1), torch.float32),
+                         self.gate_step(), self._t(beta.reshape(-1), torch.float32), y,
+                         stream_aux=stream_aux, flags=flags)
+        torch.cuda.synchronize()
+        return y.cpu().numpy().reshape(self.N, self.dv).astype(np.float64)
+
+    # ---- workload inputs in oracle layout [T][N][...]
+    def inputs(self, T, sub=0):
+        q, k, v, beta = gen.eval_inputs(self.wl, T, self.nL, self.B, sub=sub)
+        return (q.reshape(T, self.N, self.dk), k.reshape(T, self.N, self.dk), v.reshape(T, self.N, self.dv),
+                beta.reshape(T, self.N))
+
+    def warm_state(self, steps=None):
+        """Float64 unquantized warm-up from zero (the workload's warm-up length) -> float states [N, d_k, d_v]."""
+        steps = self.wl.warmup_steps if steps is None else steps
+        S = np.zeros((self.N, self.dk, self.dv))
+        if steps == 0:
+            return S
+        q, k, v, beta = gen.warmup_inputs(self.wl, steps, self.nL, self.B)
+        sh = lambda a, d: a.reshape(steps, self.N, d).astype(np.float64)
+        alpha = np.broadcast_to(self.alpha_states(), (steps,) + self.alpha_states().shape)
+        S, _ = run_unquantized(S, sh(q, self.dk), sh(k, self.dk), sh(v, self.dv), alpha, beta.reshape(steps, self.N))
+        if self.wl.ridge_rows or self.wl.ridge_cols:
+            rr, cc = gen.ridge_positions(self.wl)
+            S = S.reshape(self.nL, self.B, self.H, self.dk, self.dv)
+            for l in range(self.nL):
+                for h in range(self.H):
+                    S[l, :, h, rr[l, h], :] *= self.wl.ridge_scale
+                    S[l, :, h, :, cc[l, h]] *= self.wl.ridge_scale
+            S = S.reshape(self.N, self.dk, self.dv)
+        return S
+
+    def close(self):
+        self.pool.close()
+        self.plan.close()

@@ -1,0 +1,281 @@
+"""GPU parity: the HIP library (through the C ABI) against the float64 oracle.
+
+Teacher-forced steps import the oracle's packed state, run one library step,
+export the result and compare it with the oracle's step by the tie-aware rule
+in _parity.py.  Free-running runs compare the final readout and state.
+"""
+import numpy as np
+import pytest
+
+from oracle import quant
+from oracle.numerics import fp16_round
+from oracle.step import packed_step, run_packed
+from workloads import configs, gen
+
+from _parity import compare_step, from_canonical, to_canonical
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch(dev):
+    import torch
+    return torch
+
+
+def _rig(wl, n_layers, batch, **kw):
+    from _rig import Rig
+    return Rig(wl, n_layers, batch, **kw)
+
+
+# ---------------------------------------------------------------- codec
+
+def _random_canonical(rig, seed):
+    """Valid random codes for every row range, pivot values, and binary16 scales."""
+    g = np.random.default_rng(seed)
+    N, dk, dv = rig.N, rig.dk, rig.dv
+    bits = rig.rows.bits
+    qm = (2 ** (np.where(bits == 16, 8, bits) - 1) - 1)[:, :, None]
+    Q = g.integers(-qm, qm + 1, size=(N, dk, dv))
+    V = np.where(rig.rows.pivot[:, :, None], fp16_round(g.standard_normal((N, dk, dv)) * 3), 0.0)
+    Q = np.where(rig.rows.pivot[:, :, None], 0, Q)
+    r = fp16_round(g.uniform(0.01, 4.0, (N, dk)))
+    r = np.where(rig.rows.pivot, 1.0, r)
+    c = fp16_round(g.uniform(0.01, 4.0, (N, dv)))
+    return quant.Packed(Q=Q, r=r, c=c, V=V)
+
+
+@pytest.mark.parametrize("wl,nL,B", [(configs.TINY, 1, 1), (configs.GDN_DECODE, 1, 2),
+                                     (configs.KDA_DECODE, 1, 2), (configs.OUTLIER, 1, 1)],
+                         ids=["tiny", "gdn", "kda", "outlier"])
+def test_codec_roundtrip_and_slot_isolation(torch, wl, nL, B):
+    say(f"codec {wl.name} layers={nL} batch={B}")
+    rig = _rig(wl, nL, B, n_slots=B + 2, slots=np.arange(B, dtype=np.int32) + 1)
+    before = rig.mem.clone()
+    P = _random_canonical(rig, 1)
+    rig.import_packed(P)
+    torch.cuda.synchronize()
+    Q = rig.export_packed()
+    assert np.array_equal(Q.Q, P.Q) and np.array_equal(Q.r, P.r) and np.array_equal(Q.c, P.c)
+    assert np.array_equal(Q.V, P.V)
+    sb = rig.plan.desc["slot_bytes"]
+    after = rig.mem.cpu().numpy()
+    b0 = before.cpu().numpy()
+    assert np.array_equal(after[:sb], b0[:sb])                      # slot 0 untouched
+    assert np.array_equal(after[(B + 1) * sb:], b0[(B + 1) * sb:])  # slot B+1 untouched
+    rig.close()
+
+
+@pytest.mark.parametrize("wl,nL,B", [(configs.GDN_DECODE, 1, 2), (configs.KDA_DECODE, 1, 1),
+                                     (configs.OUTLIER, 1, 1)], ids=["gdn", "kda", "outlier"])
+def test_unpack_is_dequantize(torch, wl, nL, B):
+    say(f"unpack {wl.name}")
+    rig = _rig(wl, nL, B)
+    P = _random_canonical(rig, 2)
+    rig.import_packed(P)
+    X = torch.zeros(rig.N * rig.dk * rig.dv, dtype=torch.float32, device="cuda")
+    import quantized_delta_rule_02_amd as sq
+    sq.sq_unpack(rig.pool, 0, nL, B, rig.slots, X)
+    torch.cuda.synchronize()
+    got = X.cpu().numpy().reshape(rig.N, rig.dk, rig.dv).astype(np.float64)
+    want = quant.dequantize(P, rig.rows)
+    assert np.allclose(got, want, rtol=2 ** -22, atol=0)
+    rig.close()
+
+
+@pytest.mark.parametrize("wl,nL,B", [(configs.TINY, 1, 1), (configs.GDN_DECODE, 1, 2),
+                                     (configs.KDA_DECODE, 1, 2), (configs.OUTLIER, 1, 1)],
+                         ids=["tiny", "gdn", "kda", "outlier"])
+def test_pack_matches_quantize(torch, wl, nL, B):
+    say(f"pack {wl.name}")
+    rig = _rig(wl, nL, B)
+    X = rig.warm_state(steps=min(wl.warmup_steps, 64))
+    if not np.any(X):
+        X = np.random.default_rng(3).standard_normal(X.shape)
+    X = X.astype(np.float32).astype(np.float64)
+    import quantized_delta_rule_02_amd as sq
+    sq.sq_pack(rig.pool, 0, nL, B, rig.slots, rig._t(X.reshape(-1), torch.float32))
+    torch.cuda.synchronize()
+    Pg = rig.export_packed()
+    Pref = quant.quantize(X, rig.rows, wl.grid)
+    R = compare_step(X, np.zeros((rig.N, rig.dv)), rig.rows, wl.grid, np.zeros((rig.N, rig.dv)), Pg, Pref)
+    say(R)
+    assert R.ok(), R.failures
+    rig.close()
+
+
+# ---------------------------------------------------------------- teacher-forced steps
+
+CASES = [
+    ("tiny", configs.TINY, 1, 1, 64),
+    ("gdn", configs.GDN_DECODE, 1, 3, 4),
+    ("kda", configs.KDA_DECODE, 1, 2, 4),
+    ("serving6", configs.SERVING_6, 2, 2, 3),
+    ("serving4", configs.SERVING_4, 2, 2, 3),
+    ("outlier", configs.OUTLIER, 1, 1, 3),
+]
+
+
+@pytest.mark.parametrize("name,wl,nL,B,T", CASES, ids=[c[0] for c in CASES])
+def test_step_teacher_forced(torch, name, wl, nL, B, T):
+    say(f"step {name}: layers={nL} batch={B} steps={T}")
+    rig = _rig(wl, nL, B)
+    S0 = rig.warm_state()
+    P = quant.quantize(S0, rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(T)
+    alpha = rig.alpha_states()
+    worst = None
+    for t in range(T):
+        rig.import_packed(P)
+        y_g = rig.step(q[t], k[t], v[t], beta[t])
+        Pg = rig.export_packed()
+        P2, y, X = packed_step(P, rig.rows, q[t], k[t], v[t], alpha, beta[t], wl.grid)
+        R = compare_step(X, y, rig.rows, wl.grid, y_g, Pg, P2)
+        if worst is None or R.y_rel > worst.y_rel:
+            worst = R
+        assert R.ok(), f"step {t}: {R.failures}"
+        P = P2
+    say(name, worst)
+    rig.close()
+
+
+def test_split_arrangement_is_bitwise_fused(torch):
+    """Readout kernel on one stream, fit + pack on another: identical bytes and readout."""
+    wl = configs.GDN_DECODE
+    say("split vs fused gdn")
+    rig = _rig(wl, 1, 4)
+    P = quant.quantize(rig.warm_state(steps=64), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(2)
+    import quantized_delta_rule_02_amd as sq
+    aux = torch.cuda.Stream()
+    outs = []
+    for flags, s_aux in ((0, None), (sq.SQ_STEP_SPLIT, aux), (sq.SQ_STEP_SPLIT, None)):
+        rig.import_packed(P)
+        ys = [rig.step(q[t], k[t], v[t], beta[t], flags=flags, stream_aux=s_aux) for t in range(2)]
+        outs.append((ys, rig.mem.clone()))
+    for ys, mem in outs[1:]:
+        assert all(np.array_equal(a, b) for a, b in zip(ys, outs[0][0]))
+        assert torch.equal(mem, outs[0][1])
+    rig.close()
+
+
+def test_repeated_runs_are_deterministic(torch):
+    wl = configs.KDA_DECODE
+    say("determinism kda")
+    rig = _rig(wl, 1, 2)
+    P = quant.quantize(rig.warm_state(steps=32), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(1)
+    res = []
+    for _ in range(2):
+        rig.import_packed(P)
+        y = rig.step(q[0], k[0], v[0], beta[0])
+        res.append((y, rig.mem.clone()))
+    assert np.array_equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    rig.close()
+
+
+# ---------------------------------------------------------------- free-running drift
+
+@pytest.mark.parametrize("name,wl,nL,B,T", [("tiny", configs.TINY, 1, 1, 64), ("gdn", configs.GDN_DECODE, 1, 1, 256)],
+                         ids=["tiny", "gdn"])
+def test_free_running_drift(torch, name, wl, nL, B, T):
+    say(f"drift {name} steps={T}")
+    rig = _rig(wl, nL, B)
+    P0 = quant.quantize(rig.warm_state(), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(T)
+    alpha = np.broadcast_to(rig.alpha_states(), (T,) + rig.alpha_states().shape)
+    rig.import_packed(P0)
+    ys = [rig.step(q[t], k[t], v[t], beta[t]) for t in range(T)]
+    Pg = rig.export_packed()
+    PT, yo = run_packed(P0, rig.rows, q, k, v, alpha, beta, wl.grid)
+    y_rel = np.linalg.norm(ys[-1] - yo[-1]) / np.linalg.norm(yo[-1])
+    Xg, Xo = quant.dequantize(Pg, rig.rows), quant.dequantize(PT, rig.rows)
+    x_rel = np.linalg.norm(Xg - Xo) / np.linalg.norm(Xo)
+    say(f"drift {name}: y rel {y_rel:.3e}  state rel {x_rel:.3e}")
+    assert y_rel <= 1e-3 and x_rel <= 1e-3
+    rig.close()
+
+
+# ---------------------------------------------------------------- comparators
+
+@pytest.mark.parametrize("wl", [configs.GDN_DECODE, configs.OUTLIER], ids=["gdn", "outlier"])
+def test_int8_and_fp32_comparators(torch, wl):
+    import quantized_delta_rule_02_amd as sq
+    from oracle.recurrence import delta_update
+    from oracle.step import int8_step
+    say(f"comparators {wl.name}")
+    B, H, dk, dv = 2, wl.n_heads, wl.d_k, wl.d_v
+    n_slots = 3
+    slots = np.array([2, 0], np.int32)
+    g = np.random.default_rng(5)
+    N = B * H
+    S = (g.standard_normal((N, dk, dv)) * 2).astype(np.float32)
+    Q0, s0 = quant.int8_row_quantize(S.astype(np.float64))
+    q, k, v, beta = [a[0, 0] for a in gen.eval_inputs(wl, 1, 1, B)]
+    q, k, v, beta = q.reshape(N, dk), k.reshape(N, dk), v.reshape(N, dv), beta.reshape(N)
+    gates = gen.unit_gates(wl)[0]
+    alpha = (np.broadcast_to(gates[None], (B,) + gates.shape)).reshape((N,) if wl.form == "gdn" else (N, dk))
+    t = lambda a, dt=torch.float32: torch.tensor(np.ascontiguousarray(a), device="cuda").to(dt)
+    # pool-ordered state arrays: state index = slot * H + head
+    codes = np.zeros((n_slots * H, dk, dv), np.int8)
+    scales = np.ones((n_slots * H, dk), np.float32)
+    Sfull = np.zeros((n_slots * H, dk, dv), np.float32)
+    for b in range(B):
+        codes[slots[b] * H:(slots[b] + 1) * H] = Q0[b * H:(b + 1) * H]
+        scales[slots[b] * H:(slots[b] + 1) * H] = s0[b * H:(b + 1) * H]
+        Sfull[slots[b] * H:(slots[b] + 1) * H] = S[b * H:(b + 1) * H]
+    dc, ds, dS = t(codes, torch.int8), t(scales), t(Sfull)
+    y8 = torch.zeros(N * dv, device="cuda")
+    y32 = torch.zeros(N * dv, device="cuda")
+    form = 0 if wl.form == "gdn" else 1
+    sq.sq_int8_step(form, H, dk, dv, n_slots, 0, 1, B, t(slots, torch.int32), dc, ds, t(q), t(k), t(v),
+                    t(alpha), t(beta), y8)
+    sq.sq_fp32_step(form, H, dk, dv, n_slots, 0, 1, B, t(slots, torch.int32), dS, t(q), t(k), t(v),
+                    t(alpha), t(beta), y32)
+    torch.cuda.synchronize()
+    Q1, s1, y_ref8, X8 = int8_step(Q0, s0, q, k, v, alpha, beta)
+    X32, y_ref32 = delta_update(S.astype(np.float64), q, k, v, alpha, beta)
+    got_c = dc.cpu().numpy().reshape(n_slots * H, dk, dv)
+    got_s = ds.cpu().numpy().reshape(n_slots * H, dk)
+    got_S = dS.cpu().numpy().reshape(n_slots * H, dk, dv)
+    rows_c = np.concatenate([got_c[slots[b] * H:(slots[b] + 1) * H] for b in range(B)]).astype(np.int64)
+    rows_s = np.concatenate([got_s[slots[b] * H:(slots[b] + 1) * H] for b in range(B)]).astype(np.float64)
+    rows_S = np.concatenate([got_S[slots[b] * H:(slots[b] + 1) * H] for b in range(B)]).astype(np.float64)
+    assert np.linalg.norm(y8.cpu().numpy().reshape(N, dv) - y_ref8) / np.linalg.norm(y_ref8) < 1e-5
+    assert np.linalg.norm(y32.cpu().numpy().reshape(N, dv) - y_ref32) / np.linalg.norm(y_ref32) < 1e-5
+    assert np.allclose(rows_S, X32, rtol=1e-5, atol=1e-5 * np.abs(X32).max())
+    assert np.allclose(rows_s, s1, rtol=1e-5)
+    # codes for the library's row scales: equal except at rounding ties
+    z = X8 / rows_s[:, :, None]
+    Qz = np.clip(np.rint(z), -127, 127)
+    dq = rows_c - Qz
+    near = np.abs(np.abs(z - np.floor(z)) - 0.5) < 1e-3
+    assert np.all(np.abs(dq) <= 1) and np.all((dq == 0) | near)
+    assert np.count_nonzero(dq) <= 1e-3 * dq.size
+    assert np.array_equal(got_c[H:2 * H], codes[H:2 * H])            # slot 1 untouched
+
+
+def test_copy_kernel(torch):
+    import quantized_delta_rule_02_amd as sq
+    a = torch.randn(1 << 20, device="cuda")
+    b = torch.zeros_like(a)
+    sq.sq_copy(a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_validate_mode_rejects_bad_slots(torch):
+    import quantized_delta_rule_02_amd as sq
+    wl = configs.TINY
+    rig = _rig(wl, 1, 2, n_slots=3)
+    q, k, v, beta = rig.inputs(1)
+    for bad in ([0, 0], [0, 3], [-1, 1]):
+        rig.slots = torch.tensor(bad, dtype=torch.int32, device="cuda")
+        with pytest.raises(sq.StepQError) as e:
+            rig.step(q[0], k[0], v[0], beta[0], flags=sq.SQ_STEP_VALIDATE)
+        assert e.value.status == -4
+    rig.close()
