@@ -32,8 +32,10 @@ def build(verbose: bool = False) -> str:
     common = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
               f"-I{os.path.join(os.path.dirname(HERE), 'include')}"]
     # packed FP32 (v_pk_*_f32) is disabled for all device code
+    # IEEE mode off: no NaN arises on the step's path, and without it fmaxf/fminf compile to one
+    # v_max/v_min instead of being preceded by canonicalizing copies of their operands
     device = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-              "-munsafe-fp-atomics"]
+              "-munsafe-fp-atomics", "-mno-amdgpu-ieee", "-fno-honor-nans"]
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, src.replace(".", "_") + ".o")

@@ -391,6 +391,7 @@ static StepParams base_params(const sq_pool* pl, int32_t layer0, int32_t n_layer
     p.form = pl->form;
     p.slots = slots;
     p.n_grid = pl->n_grid;
+    p.unit_first = pl->grid[0] == 1.0f ? 1 : 0;
     for (int g = 0; g < kMaxGrid; ++g) p.grid[g] = pl->grid[g];
     return p;
 }

@@ -77,6 +77,7 @@ struct StepParams {
     float* e_buf;        // split arrangement: v - k^T D S per state [state][d_v]
     int32_t state0;      // split arrangement: first state of the chunk
     int32_t n_grid;
+    int32_t unit_first;  // grid[0] == 1: the first candidate needs no clamp
     float grid[kMaxGrid];
 };
 

@@ -25,6 +25,10 @@
 #include "internal.h"
 #include "launch.h"
 
+#ifndef STEP_WAVES_PER_EU
+#define STEP_WAVES_PER_EU 2   // minimum waves per SIMD the register allocation must allow
+#endif
+
 namespace sq {
 
 // ---------------------------------------------------------------- helpers
@@ -44,6 +48,13 @@ __device__ __forceinline__ float med3(float x, float lo, float hi) {
     return __builtin_amdgcn_fmed3f(x, lo, hi);
 }
 __device__ __forceinline__ int bias_of(int bits) { return bits == 16 ? 0 : (1 << (bits - 1)); }
+// a value every lane of the wave holds, moved to a scalar register
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+}
 
 // 16 entries of one lane in one group <-> container dwords (internal.h)
 __device__ __forceinline__ void unpack4(const uint32_t* d, float* o) {
@@ -130,25 +141,74 @@ __device__ __forceinline__ void store_dw(uint8_t* p, const uint32_t* d) {
     }
 }
 
+// Wave-level data movement for the row maximum.  v_permlane32_swap exchanges
+// rows 2-3 of its first operand with rows 0-1 of its second (rows of 16
+// lanes); v_permlane16_swap exchanges rows 1 and 3 of the first with rows 0
+// and 2 of the second.  DPP: row_ror:8 pairs lane l with l^8 inside a 16-lane
+// row, row_half_mirror pairs l with 7-(l&7) inside 8 lanes, quad_perm
+// [2,3,0,1] / [1,0,3,2] pair l with l^2 / l^1.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRor8 = 0x128;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppXor1 = 0xB1;
+
+template <int D>
+__device__ __forceinline__ float dpp_partner(float x) {
+    if constexpr (D == 8) return dpp_f<kDppRor8>(x);
+    else if constexpr (D == 4) return dpp_f<kDppHalfMirror>(x);
+    else if constexpr (D == 2) return dpp_f<kDppXor2>(x);
+    else return dpp_f<kDppXor1>(x);
+}
+
+// Sum over the 64 lanes of a wave (the result is valid in lane 0): xor-1, xor-2 and the
+// two mirrors reduce each row of 16 lanes, lane reads add the four rows.
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppHalfMirror>(x);
+    x += dpp_f<0x140>(x);   // row_mirror
+    const int xi = __float_as_int(x);
+    return (__int_as_float(__builtin_amdgcn_readlane(xi, 0)) + __int_as_float(__builtin_amdgcn_readlane(xi, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(xi, 32)) + __int_as_float(__builtin_amdgcn_readlane(xi, 48)));
+}
+
 // Transpose-reduce of per-row maxima across the LPR lanes of a row band.
-// Before: v[0..N) = this lane's partial max of local rows 0..N-1.  After:
-// v[0] = the full max of local row `row` (the same row on LPR/N lanes).
+// Before: v[0..N) = this lane's partial max of local rows 0..N-1.  Each halving
+// stage pairs every lane with a lane of the other half of a group of 2D lanes;
+// the lane keeps the half of its rows selected by its bit D and takes the
+// partner's values of those rows.  After: v[0] = the max of local row `row`
+// over all LPR lanes (LPR/N lanes hold each row).
 template <int D, int N>
 struct RowMax {
     static __device__ __forceinline__ void run(float* v, int lane, int& row) {
         if constexpr (D >= 1) {
             if constexpr (N > 1) {
                 const bool hi = (lane & D) != 0;
+                if constexpr (D == 32 || D == 16) {
 #pragma unroll
-                for (int i = 0; i < N / 2; ++i) {
-                    const float keep = hi ? v[i + N / 2] : v[i];
-                    const float send = hi ? v[i] : v[i + N / 2];
-                    v[i] = fmaxf(keep, __shfl_xor(send, D));
+                    for (int i = 0; i < N / 2; ++i) {
+                        uint32_t x = __float_as_uint(v[i]), y = __float_as_uint(v[i + N / 2]);
+                        const auto r = (D == 32) ? __builtin_amdgcn_permlane32_swap(x, y, false, false)
+                                                 : __builtin_amdgcn_permlane16_swap(x, y, false, false);
+                        v[i] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < N / 2; ++i) {
+                        const float lo = fmaxf(v[i], dpp_partner<D>(v[i]));
+                        const float up = fmaxf(v[i + N / 2], dpp_partner<D>(v[i + N / 2]));
+                        v[i] = hi ? up : lo;
+                    }
                 }
                 if (hi) row += N / 2;
                 RowMax<D / 2, N / 2>::run(v, lane, row);
             } else {
-                v[0] = fmaxf(v[0], __shfl_xor(v[0], D));
+                static_assert(D <= 8, "a butterfly across rows of 16 lanes is not needed by any shape");
+                v[0] = fmaxf(v[0], dpp_partner<D>(v[0]));
                 RowMax<D / 2, 1>::run(v, lane, row);
             }
         }
@@ -173,19 +233,166 @@ struct Shape {
 
 template <int DK, int DV>
 struct StepSmem {
-    float A[DK], nb[DK], ck[DK], cq[DK], pk[DK], pq[DK], al[DK], bk[DK];
-    float rn[DK], ir[DK], sw[DK], iq[DK], qm[DK], w[DK];
-    int rb[DK];
+    float4 acc[DK];    // column accumulation: A k, A q (code rows), alpha k, alpha q (pivot rows)
+    float4 upd[DK];    // update: A = alpha r_old, -A * bias, beta k, alpha (pivot rows)
+    float4 fit[DK];    // requantization: 1 / r_new, sqrt(w) r_new, 1 / qmax, qmax
+    float2 fin[DK];    // final rounding bounds: magic + container bias -/+ qmax
+    float rn[DK];      // new binary16 row factor
+    float w[DK];
+    int rb[DK];        // code width of the row (16 = pivot)
     float part[Shape<DK, DV>::NW][4][DV];
     float red[Shape<DK, DV>::NW][4];
 };
 
-template <int DK, int DV, int MODE>
-__global__ void __launch_bounds__(nw_of(DK, DV) * 64)
+constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23: x + kMagic rounds x to an integer in the low mantissa bits
+
+// byte 0 of four registers -> one dword
+__device__ __forceinline__ uint32_t gather4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3) {
+    const uint32_t a = __builtin_amdgcn_perm(r1, r0, 0x0C0C0400u);
+    const uint32_t b = __builtin_amdgcn_perm(r3, r2, 0x0C0C0400u);
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+
+// fast unpack of one lane's 16 biased codes to float (layout in internal.h)
+__device__ __forceinline__ void unpack4f(const uint32_t* d, float* o) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const uint32_t lo = d[w] & 0x0F0F0F0Fu, hi = (d[w] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            o[8 * w + k] = (float)((lo >> (8 * k)) & 0xFFu);
+            o[8 * w + 4 + k] = (float)((hi >> (8 * k)) & 0xFFu);
+        }
+    }
+}
+__device__ __forceinline__ void unpack6f(const uint32_t* d, float* o) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        const uint32_t x = d[w] & 0x3F3F3F3Fu;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[4 * w + k] = (float)((x >> (8 * k)) & 0xFFu);
+    }
+    const uint32_t t0 = d[0] >> 6, t1 = d[1] >> 4, t2 = d[2] >> 2;
+    uint32_t p = (t0 & 0x03030303u) | (t1 & ~0x03030303u);
+    p = (p & 0x0F0F0F0Fu) | (t2 & ~0x0F0F0F0Fu);
+    p &= 0x3F3F3F3Fu;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[12 + k] = (float)((p >> (8 * k)) & 0xFFu);
+}
+
+// pack 16 magic-rounded codes (the code sits in the low bits of each float's pattern)
+__device__ __forceinline__ void pack4m(const float* m, uint32_t* d) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const uint32_t lo = gather4(__float_as_uint(m[8 * w]), __float_as_uint(m[8 * w + 1]),
+                                    __float_as_uint(m[8 * w + 2]), __float_as_uint(m[8 * w + 3]));
+        const uint32_t hi = gather4(__float_as_uint(m[8 * w + 4]), __float_as_uint(m[8 * w + 5]),
+                                    __float_as_uint(m[8 * w + 6]), __float_as_uint(m[8 * w + 7]));
+        d[w] = lo | (hi << 4);
+    }
+}
+__device__ __forceinline__ void pack6m(const float* m, uint32_t* d) {
+    const uint32_t p = gather4(__float_as_uint(m[12]), __float_as_uint(m[13]), __float_as_uint(m[14]),
+                               __float_as_uint(m[15]));
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        const uint32_t b = gather4(__float_as_uint(m[4 * w]), __float_as_uint(m[4 * w + 1]),
+                                   __float_as_uint(m[4 * w + 2]), __float_as_uint(m[4 * w + 3]));
+        d[w] = ((p << (6 - 2 * w)) & 0xC0C0C0C0u) | b;
+    }
+}
+__device__ __forceinline__ void pack8m(const float* m, uint32_t* d) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        d[w] = gather4(__float_as_uint(m[4 * w]), __float_as_uint(m[4 * w + 1]), __float_as_uint(m[4 * w + 2]),
+                       __float_as_uint(m[4 * w + 3]));
+}
+
+template <int NDW>
+__device__ __forceinline__ void load_group(const uint8_t* gp, int lane, bool act, uint32_t* d) {
+    if (act) load_dw<NDW>(gp + lane * 4 * NDW, d);
+    else {
+#pragma unroll
+        for (int i = 0; i < NDW; ++i) d[i] = 0;
+    }
+}
+
+// One LDS round of the column fit: KG candidates c = binary16(gamma * c0), the
+// impact-weighted error F = c^2 sum_i (sqrt(w_i) r_i)^2 (t_ij / c - Q_ij)^2 of the
+// wave's rows, combined over the waves; the best candidate so far is kept (strict <).
+template <class Sh, int KG, bool FREE0, class Smem>
+__device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float* c0, const float* grid, int g0,
+                                           int n_grid, int wave, int lane, bool act, float* cbest, float* fbest) {
+    constexpr int CPL = Sh::CPL, RPW = Sh::RPW, NW = Sh::NW;
+    const int col0 = lane * CPL;
+    float cg[KG][CPL], icg[KG][CPL], Fp[KG][CPL];
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+        const float gam = grid[min(g0 + j, n_grid - 1)];   // a short last round repeats a candidate
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            cg[j][c] = scale_fp16(gam * c0[c]);
+            icg[j][c] = __builtin_amdgcn_rcpf(cg[j][c]);
+            Fp[j][c] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        // two rows at a time: an empty asm "redefines" the inverse scales, so later rows' candidate
+        // chains cannot be hoisted above it (interleaving all rows costs registers, not speed)
+        if (r % 2 == 0) {
+#pragma unroll
+            for (int j = 0; j < KG; ++j)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) __asm__ volatile("" : "+v"(icg[j][c]));
+        }
+        const float4 f = sm.fit[wave * RPW + r];
+        const float qm = f.w, sw = f.y;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float t = X[r * CPL + c];
+#pragma unroll
+            for (int j = 0; j < KG; ++j) {
+                const float R = rintf(t * icg[j][c]);
+                const float Qc = (FREE0 && j == 0) ? R : med3(R, -qm, qm);
+                const float dd = sw * fmaf(t, icg[j][c], -Qc);
+                Fp[j][c] = fmaf(dd, dd, Fp[j][c]);
+            }
+        }
+    }
+    if (act) {
+#pragma unroll
+        for (int j = 0; j < KG; ++j)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) sm.part[wave][j][col0 + c] = Fp[j][c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            float F = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) F += act ? sm.part[w][j][col0 + c] : 0.f;
+            F *= cg[j][c] * cg[j][c];
+            if (F < fbest[c]) {
+                fbest[c] = F;
+                cbest[c] = cg[j][c];
+            }
+        }
+    }
+    __syncthreads();
+}
+
+template <int DK, int DV, int MODE, int KG>
+__global__ void __launch_bounds__(nw_of(DK, DV) * 64, STEP_WAVES_PER_EU)
 k_state(StepParams a) {
     using Sh = Shape<DK, DV>;
     constexpr int CPL = Sh::CPL, LPR = Sh::LPR, GR = Sh::GR, RPW = Sh::RPW, NW = Sh::NW;
     constexpr int GPW = Sh::GPW, EPL = Sh::EPL, NG = Sh::NG;
+    constexpr bool kNeedOld = (MODE != kModePack);
+    constexpr bool kUpdate = (MODE == kModeStep || MODE == kModeSplitA || MODE == kModeSplitB);
+    constexpr bool kAccum = (MODE == kModeStep || MODE == kModeSplitA);
     __shared__ StepSmem<DK, DV> sm;
 
     const int sid = blockIdx.x + a.state0;
@@ -193,19 +400,42 @@ k_state(StepParams a) {
     const int b = (sid / a.n_heads) % a.batch;
     const int l = a.layer0 + sid / (a.n_heads * a.batch);
     const int lh = l * a.n_heads + h;
-    const int slot = a.slots[b];
-    uint8_t* rec = a.pool + (uint64_t)slot * a.slot_bytes + a.t.rec_off[lh];
-    uint16_t* rs = reinterpret_cast<uint16_t*>(rec + a.t.scale_off[lh]);   // row factors, then column scales
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // per-state table values are the same for every lane: keep them in scalar registers so that
+    // the width dispatch below is a uniform branch
+    const int slot = uniform(a.slots[b]);
+    uint8_t* rec = a.pool + (uint64_t)slot * a.slot_bytes + uniform64(a.t.rec_off[lh]);
+    uint16_t* rs = reinterpret_cast<uint16_t*>(rec + uniform(a.t.scale_off[lh]));   // row factors, then column scales
+    const int tid = threadIdx.x, wave = uniform(threadIdx.x >> 6), lane = tid & 63;
     const bool act = lane < LPR;
     const int col0 = lane * CPL;
     const uint8_t* gbits = a.t.grp_bits + (size_t)lh * NG;
     const uint32_t* goff = a.t.grp_off + (size_t)lh * NG;
-    const uint8_t hflags = a.t.head_flags[lh];
+    const int hflags = uniform(a.t.head_flags[lh]);
+
+    // ---- issue the loads of this wave's packed groups first; they overlap phase 0.  Every lane
+    // loads 4 dwords at its stride 2b bytes: a 4- or 6-bit lane over-reads into its neighbour's
+    // data (or the record's scale vectors after the last group), a 16-bit lane gets its first half.
+    uint32_t raw[GPW][4];
+    int gb[GPW];
+#pragma unroll
+    for (int g = 0; g < GPW; ++g) {
+        gb[g] = uniform(gbits[wave * GPW + g]);
+        if constexpr (MODE != kModePack) {
+            const uint8_t* gp = rec + uniform(goff[wave * GPW + g]);
+            if (act) load_dw<4>(gp + lane * 2 * gb[g], raw[g]);
+            else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) raw[g][i] = 0;
+            }
+        }
+    }
+    float c_old[CPL];
+    if constexpr (kNeedOld) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) c_old[c] = act ? h2f(rs[DK + col0 + c]) : 1.f;
+    }
 
     // ---- phase 0: per-row coefficients (one thread per storage row)
-    constexpr bool kNeedOld = (MODE != kModePack);
-    constexpr bool kUpdate = (MODE == kModeStep || MODE == kModeSplitA || MODE == kModeSplitB);
     float kq_part = 0.f, kb_part = 0.f, qb_part = 0.f;
     if (tid < DK) {
         const int t = tid;
@@ -226,26 +456,17 @@ k_state(StepParams a) {
             }
             const float A = piv ? 0.f : al * rold;
             const float bias = (float)bias_of(sb);
-            sm.A[t] = A;
-            sm.nb[t] = -A * bias;
-            sm.ck[t] = A * kk;
-            sm.cq[t] = A * qq;
-            sm.pk[t] = piv ? al * kk : 0.f;
-            sm.pq[t] = piv ? al * qq : 0.f;
-            sm.al[t] = piv ? al : 0.f;
-            sm.bk[t] = bt * kk;
+            sm.acc[t] = make_float4(A * kk, A * qq, piv ? al * kk : 0.f, piv ? al * qq : 0.f);
+            sm.upd[t] = make_float4(A, -A * bias, bt * kk, piv ? al : 0.f);
             kq_part = kk * qq;
             kb_part = A * kk * bias;
             qb_part = A * qq * bias;
         }
     }
-    if constexpr (kUpdate) {
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) {
-            kq_part += __shfl_xor(kq_part, d);
-            kb_part += __shfl_xor(kb_part, d);
-            qb_part += __shfl_xor(qb_part, d);
-        }
+    if constexpr (kAccum) {
+        kq_part = wave_sum(kq_part);
+        kb_part = wave_sum(kb_part);
+        qb_part = wave_sum(qb_part);
         if (lane == 0) {
             sm.red[wave][0] = kq_part;
             sm.red[wave][1] = kb_part;
@@ -255,13 +476,8 @@ k_state(StepParams a) {
     __syncthreads();
 
     float X[EPL];
-    float c_old[CPL];
-    if constexpr (kNeedOld) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) c_old[c] = act ? h2f(rs[DK + col0 + c]) : 1.f;
-    }
 
-    // ---- phase 1: load + unpack (biased codes / pivot values), column accumulations
+    // ---- phase 1: unpack (biased codes / pivot values), column accumulations k^T D S, q^T D S
     if constexpr (MODE == kModePack) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -275,48 +491,42 @@ k_state(StepParams a) {
         for (int c = 0; c < CPL; ++c) U1[c] = P1[c] = U2[c] = P2[c] = 0.f;
 #pragma unroll
         for (int g = 0; g < GPW; ++g) {
-            const int gg = wave * GPW + g;
-            const int sb = gbits[gg];
-            const uint8_t* gp = rec + goff[gg];
             float* xg = &X[16 * g];
-            uint32_t d[8];
-            if (sb == 4) {
-                if (act) load_dw<2>(gp + lane * 8, d); else d[0] = d[1] = 0;
-                unpack4(d, xg);
-            } else if (sb == 6) {
-                if (act) load_dw<3>(gp + lane * 12, d); else d[0] = d[1] = d[2] = 0;
-                unpack6(d, xg);
-            } else if (sb == 8) {
-                if (act) load_dw<4>(gp + lane * 16, d); else d[0] = d[1] = d[2] = d[3] = 0;
-                unpack8(d, xg);
-            } else {
-                if (act) load_dw<8>(gp + lane * 32, d);
-                else {
+            if (gb[g] == 4) unpack4f(raw[g], xg);
+            else if (gb[g] == 6) unpack6f(raw[g], xg);
+            else if (gb[g] == 8) unpack8(raw[g], xg);
+            else {
+                uint32_t d16[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) d[i] = 0;
-                }
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int t = wave * RPW + 16 * g / CPL + e / CPL;
-                    const uint32_t bits = (d[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                    xg[e] = (sm.rb[t] == 16) ? h2f(bits) : (float)(int16_t)bits;
-                }
-            }
-            if constexpr (MODE == kModeStep || MODE == kModeSplitA) {
+                for (int i = 0; i < 4; ++i) d16[i] = raw[g][i];
+                if (act) load_dw<4>(rec + uniform(goff[wave * GPW + g]) + lane * 32 + 16, d16 + 4);
+                else d16[4] = d16[5] = d16[6] = d16[7] = 0;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int t = wave * RPW + (16 * g + e) / CPL;
-                    const int c = e % CPL;
-                    U1[c] = fmaf(sm.ck[t], xg[e], U1[c]);
-                    P1[c] = fmaf(sm.cq[t], xg[e], P1[c]);
+                    const uint32_t bits = (d16[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    xg[e] = (sm.rb[t] == 16) ? h2f(bits) : (float)(int16_t)bits;
                 }
-                if (sb == 16) {
+            }
+            if constexpr (kAccum) {
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int t = wave * RPW + (16 * g + e) / CPL;
-                        const int c = e % CPL;
-                        U2[c] = fmaf(sm.pk[t], xg[e], U2[c]);
-                        P2[c] = fmaf(sm.pq[t], xg[e], P2[c]);
+                for (int r = 0; r < GR; ++r) {
+                    const float2 cf = *reinterpret_cast<const float2*>(&sm.acc[wave * RPW + g * GR + r]);
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        U1[c] = fmaf(cf.x, xg[r * CPL + c], U1[c]);
+                        P1[c] = fmaf(cf.y, xg[r * CPL + c], P1[c]);
+                    }
+                }
+                if (gb[g] == 16) {
+#pragma unroll
+                    for (int r = 0; r < GR; ++r) {
+                        const float4 cf = sm.acc[wave * RPW + g * GR + r];
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) {
+                            U2[c] = fmaf(cf.z, xg[r * CPL + c], U2[c]);
+                            P2[c] = fmaf(cf.w, xg[r * CPL + c], P2[c]);
+                        }
                     }
                 }
             }
@@ -328,8 +538,9 @@ k_state(StepParams a) {
             for (int e = 0; e < EPL; ++e) {
                 const int t = wave * RPW + e / CPL;
                 const int c = e % CPL;
+                const float4 u = sm.upd[t];
                 const bool piv = sm.rb[t] == 16;
-                const float s = piv ? X[e] : c_old[c] * fmaf(sm.A[t], X[e], sm.nb[t]);
+                const float s = piv ? X[e] : c_old[c] * fmaf(u.x, X[e], u.y);
                 const int i = a.t.perm[(size_t)lh * DK + t];
                 if (act) a.x_out[((size_t)sid * DK + i) * DV + col0 + c] = s;
             }
@@ -337,7 +548,7 @@ k_state(StepParams a) {
         }
 
         float ecol[CPL];
-        if constexpr (MODE == kModeStep || MODE == kModeSplitA) {
+        if constexpr (kAccum) {
             if (act) {
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
@@ -387,22 +598,28 @@ k_state(StepParams a) {
         // ---- phase 2: the updated float state X = D S + beta k e^T in registers
 #pragma unroll
         for (int g = 0; g < GPW; ++g) {
-            const int sb = gbits[wave * GPW + g];
-            if (sb != 16) {
+            if (gb[g] != 16) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int t = wave * RPW + (16 * g + e) / CPL;
-                    const int c = e % CPL;
-                    X[16 * g + e] = fmaf(c_old[c], fmaf(sm.A[t], X[16 * g + e], sm.nb[t]), sm.bk[t] * ecol[c]);
+                for (int r = 0; r < GR; ++r) {
+                    const float4 u = sm.upd[wave * RPW + g * GR + r];
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        const int e = 16 * g + r * CPL + c;
+                        X[e] = fmaf(c_old[c], fmaf(u.x, X[e], u.y), u.z * ecol[c]);
+                    }
                 }
             } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int t = wave * RPW + (16 * g + e) / CPL;
-                    const int c = e % CPL;
+                for (int r = 0; r < GR; ++r) {
+                    const int t = wave * RPW + g * GR + r;
+                    const float4 u = sm.upd[t];
                     const bool piv = sm.rb[t] == 16;
-                    const float dq = piv ? sm.al[t] * X[16 * g + e] : c_old[c] * (sm.A[t] * X[16 * g + e]);
-                    X[16 * g + e] = fmaf(sm.bk[t], ecol[c], dq);
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        const int e = 16 * g + r * CPL + c;
+                        const float dq = piv ? u.w * X[e] : c_old[c] * (u.x * X[e]);
+                        X[e] = fmaf(u.z, ecol[c], dq);
+                    }
                 }
             }
         }
@@ -413,9 +630,9 @@ k_state(StepParams a) {
         float rm[RPW];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-            float m = 0.f;
+            float m = fabsf(X[r * CPL]);
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) m = fmaxf(m, fabsf(X[r * CPL + c]));
+            for (int c = 1; c < CPL; ++c) m = fmaxf(m, fabsf(X[r * CPL + c]));
             rm[r] = act ? m : 0.f;
         }
         int row = 0;
@@ -427,13 +644,13 @@ k_state(StepParams a) {
             const float m = rm[0];
             const float w = sm.w[t];
             float rn = 1.f;
-            if (!piv && m > 0.f) rn = scale_fp16(sqrtf(m / w));
+            if (!piv && m > 0.f) rn = scale_fp16(__builtin_sqrtf(m * __builtin_amdgcn_rcpf(w)));
             const float qmax = piv ? 0.f : (float)((1 << (rbits - 1)) - 1);
             sm.rn[t] = rn;
-            sm.ir[t] = 1.f / rn;
-            sm.sw[t] = piv ? 0.f : sqrtf(w) * rn;
-            sm.iq[t] = piv ? 0.f : 1.f / qmax;
-            sm.qm[t] = qmax;
+            sm.fit[t] = make_float4(__builtin_amdgcn_rcpf(rn), piv ? 0.f : __builtin_sqrtf(w) * rn,
+                                    piv ? 0.f : __builtin_amdgcn_rcpf(qmax), qmax);
+            const float mb = kMagic + (float)bias_of(gbits[t / GR]);
+            sm.fin[t] = make_float2(mb - qmax, mb + qmax);
         }
     }
     __syncthreads();
@@ -445,11 +662,32 @@ k_state(StepParams a) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) c0p[c] = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int t = wave * RPW + e / CPL;
-            const int c = e % CPL;
-            X[e] = X[e] * sm.ir[t];
-            c0p[c] = fmaxf(c0p[c], fabsf(X[e]) * sm.iq[t]);
+        for (int r = 0; r < RPW; ++r) {
+            const float ir = sm.fit[wave * RPW + r].x;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) X[r * CPL + c] *= ir;
+        }
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) {
+            const int t0 = wave * RPW + g * GR;
+            // rows are sorted by width, so a group whose first and last rows agree has one qmax
+            if (sm.rb[t0] == sm.rb[t0 + GR - 1]) {
+                const float iq = sm.fit[t0].z;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    float mg = 0.f;
+#pragma unroll
+                    for (int r = 0; r < GR; ++r) mg = fmaxf(mg, fabsf(X[16 * g + r * CPL + c]));
+                    c0p[c] = fmaxf(c0p[c], mg * iq);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < GR; ++r) {
+                    const float iq = sm.fit[t0 + r].z;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) c0p[c] = fmaxf(c0p[c], fabsf(X[16 * g + r * CPL + c]) * iq);
+                }
+            }
         }
         if (act) {
 #pragma unroll
@@ -466,7 +704,7 @@ k_state(StepParams a) {
         __syncthreads();   // part[] is reused below
     }
 
-    // ---- phase 5: column fit over the candidate grid, up to four candidates per LDS round
+    // ---- phase 5: column fit over the candidate grid, KG candidates per LDS round
     float cbest[CPL], fbest[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
@@ -474,101 +712,52 @@ k_state(StepParams a) {
         fbest[c] = __builtin_inff();
     }
     if (hflags & kHasCodeRows) {
-        for (int g0 = 0; g0 < a.n_grid; g0 += 4) {
-            const int ng = min(4, a.n_grid - g0);
-            float cg[4][CPL], icg[4][CPL], Fp[4][CPL];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const float gam = (j < ng) ? a.grid[g0 + j] : 1.f;
-                    cg[j][c] = scale_fp16(gam * c0[c]);
-                    icg[j][c] = 1.f / cg[j][c];
-                    Fp[j][c] = 0.f;
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const int t = wave * RPW + e / CPL;
-                const int c = e % CPL;
-                const float qm = sm.qm[t], sw = sm.sw[t];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (j < ng) {
-                        const float Qc = med3(rintf(X[e] * icg[j][c]), -qm, qm);
-                        const float dd = sw * fmaf(X[e], icg[j][c], -Qc);
-                        Fp[j][c] = fmaf(dd, dd, Fp[j][c]);
-                    }
-                }
-            }
-            if (act) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) sm.part[wave][j][col0 + c] = Fp[j][c];
-            }
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j < ng) {
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) {
-                        float F = 0.f;
-#pragma unroll
-                        for (int w = 0; w < NW; ++w) F += act ? sm.part[w][j][col0 + c] : 0.f;
-                        F *= cg[j][c] * cg[j][c];
-                        if (F < fbest[c]) {
-                            fbest[c] = F;
-                            cbest[c] = cg[j][c];
-                        }
-                    }
-                }
-            }
-            __syncthreads();
-        }
+        const int n_grid = a.n_grid;
+        // with gamma = 1 no code can leave its range (|X / r| <= qmax c0 and the stored c rounds c0),
+        // so the first round skips the clamp of its first candidate when grid[0] == 1
+        if (a.unit_first) grid_round<Sh, KG, true>(sm, X, c0, a.grid, 0, n_grid, wave, lane, act, cbest, fbest);
+        else grid_round<Sh, KG, false>(sm, X, c0, a.grid, 0, n_grid, wave, lane, act, cbest, fbest);
+        for (int g0 = KG; g0 < n_grid; g0 += KG)
+            grid_round<Sh, KG, false>(sm, X, c0, a.grid, g0, n_grid, wave, lane, act, cbest, fbest);
     }
     float ic[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         if (!(c0[c] > 0.f)) cbest[c] = 1.f;      // all-zero column: scale 1, zero codes
-        ic[c] = 1.f / cbest[c];
+        ic[c] = __builtin_amdgcn_rcpf(cbest[c]);
     }
 
-    // ---- phase 6: round, pack and write back codes, row factors and column scales
+    // ---- phase 6: round (magic-number RNE + clamp), pack and write back codes, row factors, column scales
 #pragma unroll
     for (int g = 0; g < GPW; ++g) {
         const int gg = wave * GPW + g;
-        const int sb = gbits[gg];
-        uint8_t* gp = rec + goff[gg];
-        int code[16];
+        const int sb = gb[g];
+        uint8_t* gp = rec + uniform(goff[gg]);
         uint32_t d[8];
-        if (sb != 16) {
-            const int bias = bias_of(sb);
+        float m[16];
+        const float mb = kMagic + (float)bias_of(sb);
+#pragma unroll
+        for (int r = 0; r < GR; ++r) {
+            const float2 bd = sm.fin[wave * RPW + g * GR + r];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int e = r * CPL + c;
+                m[e] = med3(fmaf(X[16 * g + e], ic[c], mb), bd.x, bd.y);
+            }
+        }
+        if (sb == 4) { pack4m(m, d); if (act) store_dw<2>(gp + lane * 8, d); }
+        else if (sb == 6) { pack6m(m, d); if (act) store_dw<3>(gp + lane * 12, d); }
+        else if (sb == 8) { pack8m(m, d); if (act) store_dw<4>(gp + lane * 16, d); }
+        else {
+            uint32_t hv[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int t = wave * RPW + (16 * g + e) / CPL;
-                const int c = e % CPL;
-                const float qm = sm.qm[t];
-                code[e] = (int)med3(rintf(X[16 * g + e] * ic[c]), -qm, qm) + bias;
-            }
-            if (act) {
-                if (sb == 4) { pack4(code, d); store_dw<2>(gp + lane * 8, d); }
-                else if (sb == 6) { pack6(code, d); store_dw<3>(gp + lane * 12, d); }
-                else { pack8(code, d); store_dw<4>(gp + lane * 16, d); }
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int t = wave * RPW + (16 * g + e) / CPL;
-                const int c = e % CPL;
-                const float qm = sm.qm[t];
-                const bool piv = sm.rb[t] == 16;
-                const uint32_t bits = piv ? f2h_bits(fminf(fmaxf(X[16 * g + e], -65504.f), 65504.f))
-                                          : ((uint32_t)(int)med3(rintf(X[16 * g + e] * ic[c]), -qm, qm) & 0xFFFFu);
-                code[e] = (int)bits;
+                hv[e] = (sm.rb[t] == 16) ? f2h_bits(fminf(fmaxf(X[16 * g + e], -65504.f), 65504.f))
+                                         : __float_as_uint(m[e]);
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) d[i] = (uint32_t)code[2 * i] | ((uint32_t)code[2 * i + 1] << 16);
+            for (int i = 0; i < 8; ++i) d[i] = __builtin_amdgcn_perm(hv[2 * i + 1], hv[2 * i], 0x05040100u);
             if (act) store_dw<8>(gp + lane * 32, d);
         }
     }
@@ -805,18 +994,27 @@ __global__ void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, s
 
 // ---------------------------------------------------------------- launchers
 
-template <int DK, int DV>
-static hipError_t launch_state_t(int mode, const StepParams& p, int n_states, hipStream_t s) {
+template <int DK, int DV, int KG>
+static hipError_t launch_state_kg(int mode, const StepParams& p, int n_states, hipStream_t s) {
     const dim3 blk(Shape<DK, DV>::NW * 64);
     switch (mode) {
-        case kModeStep: k_state<DK, DV, kModeStep><<<n_states, blk, 0, s>>>(p); break;
-        case kModePack: k_state<DK, DV, kModePack><<<n_states, blk, 0, s>>>(p); break;
-        case kModeUnpack: k_state<DK, DV, kModeUnpack><<<n_states, blk, 0, s>>>(p); break;
-        case kModeSplitA: k_state<DK, DV, kModeSplitA><<<n_states, blk, 0, s>>>(p); break;
-        case kModeSplitB: k_state<DK, DV, kModeSplitB><<<n_states, blk, 0, s>>>(p); break;
+        case kModeStep: k_state<DK, DV, kModeStep, KG><<<n_states, blk, 0, s>>>(p); break;
+        case kModePack: k_state<DK, DV, kModePack, KG><<<n_states, blk, 0, s>>>(p); break;
+        case kModeUnpack: k_state<DK, DV, kModeUnpack, 1><<<n_states, blk, 0, s>>>(p); break;
+        case kModeSplitA: k_state<DK, DV, kModeSplitA, 1><<<n_states, blk, 0, s>>>(p); break;
+        case kModeSplitB: k_state<DK, DV, kModeSplitB, KG><<<n_states, blk, 0, s>>>(p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// candidates per LDS round: one or two when the grid is that small, otherwise four
+// (a last round with fewer candidates repeats the final one, which cannot change the choice)
+template <int DK, int DV>
+static hipError_t launch_state_t(int mode, const StepParams& p, int n_states, hipStream_t s) {
+    if (p.n_grid == 1) return launch_state_kg<DK, DV, 1>(mode, p, n_states, s);
+    if (p.n_grid == 2) return launch_state_kg<DK, DV, 2>(mode, p, n_states, s);
+    return launch_state_kg<DK, DV, 4>(mode, p, n_states, s);
 }
 
 #define SQ_SHAPES(X) X(16, 16) X(64, 64) X(128, 128) X(128, 256)
