@@ -5,8 +5,10 @@ oracle's own float64 value sits at a rounding boundary (a "tie" within the
 library's float32 arithmetic):
   * a binary16 row factor or column scale one step away from the oracle's, when
     the oracle's pre-rounding value lies within `scale_tie` (relative) of the
-    boundary between the two; a pivot value one step away when the oracle's value
-    lies within `pivot_tie` times the row's largest magnitude of that boundary;
+    boundary between the two;
+  * a binary16 pivot value that is the rounding of some real within the forward
+    error bound of a float32 evaluation of the update (`x_err`, from
+    `step_error_bound`; without it, `pivot_tie` times the row's largest magnitude);
   * a column-scale candidate other than the oracle's choice, when its objective
     (evaluated by the oracle) is within `fit_tie` (relative) of the minimum;
   * a code one level away from the oracle's code for the library's scales, when
@@ -45,6 +47,31 @@ def from_canonical(codes, r, c, rows: quant.RowPlan) -> quant.Packed:
                         c=fp16_from_bits(np.asarray(c).view(np.uint16)), V=V)
 
 
+def step_error_bound(P0: quant.Packed, rows: quant.RowPlan, k, v, alpha, beta, bias=128.0):
+    """Per-entry bound on |X_float32 - X| for X = D S + beta k (v^T - k^T D S).
+
+    Whatever the summation order, a float32 evaluation that adds n terms errs by at most
+    gamma_n = n u / (1 - n u) times the sum of the terms' magnitudes (u = 2^-24).  The sum
+    counted here covers every term the library adds: alpha_i S_ij, and beta k_i times
+    |v_j| + sum_m |alpha_m k_m| (|S_mj| + bias r_m c_j), the codes of code rows being stored
+    with an offset of at most `bias` levels.  n is d_k plus a margin for the few products
+    and sums around the column reduction.
+    """
+    S = quant.dequantize(P0, rows)
+    N, dk, dv = S.shape
+    a = np.asarray(alpha, np.float64)
+    a = a[:, None] if a.ndim == 1 else a                      # [N, dk]
+    k = np.asarray(k, np.float64)
+    b = np.asarray(beta, np.float64)[:, None]
+    code = (~np.asarray(rows.pivot)).astype(np.float64)       # [N, dk]
+    off = bias * code[:, :, None] * P0.r[:, :, None] * P0.c[:, None, :]
+    col = np.abs(np.asarray(v, np.float64)) + np.einsum('nm,nmj->nj', np.abs(a * k), np.abs(S) + off)
+    M = np.abs(a[:, :, None] * S) + np.abs(b * k)[:, :, None] * col[:, None, :]
+    n = dk + 16
+    u = 2.0 ** -24
+    return (n * u / (1 - n * u)) * M
+
+
 def _spacing16(x):
     return np.spacing(np.abs(np.asarray(x, np.float64)).astype(np.float16)).astype(np.float64)
 
@@ -76,8 +103,9 @@ class Report:
 
 def compare_step(X, y_ref, rows: quant.RowPlan, grid, y_gpu, P_gpu: quant.Packed, P_ref: quant.Packed,
                  y_tol=1e-4, scale_tie=1e-5, fit_tie=1e-5, code_tie=1e-3, max_code_ties=1e-3,
-                 xhat_tol=1e-4, pivot_tie=2e-6) -> Report:
-    """X, y_ref: the oracle's float state and readout for the step; P_ref its packed result."""
+                 xhat_tol=1e-4, pivot_tie=2e-6, x_err=None) -> Report:
+    """X, y_ref: the oracle's float state and readout for the step; P_ref its packed result;
+    x_err: optional per-entry bound on the library's float32 error in X (step_error_bound)."""
     R = Report(n_states=X.shape[0])
     piv = np.asarray(rows.pivot)
     code_row = ~piv
@@ -135,12 +163,14 @@ def compare_step(X, y_ref, rows: quant.RowPlan, grid, y_gpu, P_gpu: quant.Packed
     if np.any(piv):
         want = fp16_round(X)
         bad_v = (P_gpu.V != want) & piv[:, :, None]
-        # a pivot entry is a float32 sum of terms of the row's magnitude: its absolute error scales
-        # with the row maximum, not with the entry (small entries come from cancellation)
-        row_mag = np.max(np.abs(X), axis=2, keepdims=True)
-        mid = 0.5 * (P_gpu.V + want)
-        adjacent = np.abs(P_gpu.V - want) <= np.maximum(_spacing16(P_gpu.V), _spacing16(want)) * 1.0001
-        tie_v = bad_v & adjacent & (np.abs(X - mid) <= pivot_tie * row_mag + scale_tie * np.abs(X))
+        if x_err is None:
+            # a pivot entry is a float32 sum of terms of the row's magnitude: its absolute error
+            # scales with the row maximum, not with the entry (small entries come from cancellation)
+            x_err = pivot_tie * np.max(np.abs(X), axis=2, keepdims=True)
+        d = x_err + scale_tie * np.abs(X)
+        # binary16 rounding is monotone: the roundings of [X - d, X + d] are exactly the values between
+        # the roundings of its ends
+        tie_v = bad_v & (P_gpu.V >= fp16_round(X - d)) & (P_gpu.V <= fp16_round(X + d))
         R.pivot_ties = int(tie_v.sum())
         if np.any(bad_v & ~tie_v):
             idx = np.argwhere(bad_v & ~tie_v)[0]

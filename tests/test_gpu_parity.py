@@ -12,7 +12,7 @@ from oracle.numerics import fp16_round
 from oracle.step import packed_step, run_packed
 from workloads import configs, gen
 
-from _parity import compare_step, from_canonical, to_canonical
+from _parity import compare_step, from_canonical, step_error_bound, to_canonical
 
 pytestmark = pytest.mark.gpu
 
@@ -134,7 +134,8 @@ def test_step_teacher_forced(torch, name, wl, nL, B, T):
         y_g = rig.step(q[t], k[t], v[t], beta[t])
         Pg = rig.export_packed()
         P2, y, X = packed_step(P, rig.rows, q[t], k[t], v[t], alpha, beta[t], wl.grid)
-        R = compare_step(X, y, rig.rows, wl.grid, y_g, Pg, P2)
+        R = compare_step(X, y, rig.rows, wl.grid, y_g, Pg, P2,
+                         x_err=step_error_bound(P, rig.rows, k[t], v[t], alpha, beta[t]))
         if worst is None or R.y_rel > worst.y_rel:
             worst = R
         assert R.ok(), f"step {t}: {R.failures}"
