@@ -7,6 +7,10 @@
 //   * the column reductions k^T D S, q^T D S, the column base and the fit
 //     objective accumulate in registers, then across the NW waves through LDS,
 //   * the row maximum is the one cross-lane reduction (transpose-reduce).
+// Per-row quantities (coefficients, row factors, rounding bounds) are computed
+// by the wave that owns the row and live in LDS only for that wave, so the
+// waves of a state meet at a workgroup barrier only for the three column
+// reductions (k^T D S and q^T D S, the column base, the fit objective).
 // The state never leaves registers between the unpack and the pack: HBM sees
 // the packed codes and scales once in each direction plus q, k, v, gate, beta, y.
 // See internal.h for the record layout.
@@ -54,6 +58,14 @@ __device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__bui
 __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
     return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+}
+
+// Orders this wave's LDS writes before its later LDS reads (other lanes' values of the
+// same wave); no other wave takes part.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // 16 entries of one lane in one group <-> container dwords (internal.h)
@@ -240,7 +252,8 @@ struct StepSmem {
     float rn[DK];      // new binary16 row factor
     float w[DK];
     int rb[DK];        // code width of the row (16 = pivot)
-    float part[Shape<DK, DV>::NW][4][DV];
+    float part[Shape<DK, DV>::NW][4][DV];   // column sums of k^T D S, q^T D S; later the fit objective
+    float cmax[Shape<DK, DV>::NW][DV];      // column base partial maxima
     float red[Shape<DK, DV>::NW][4];
 };
 
@@ -320,6 +333,7 @@ __device__ __forceinline__ void load_group(const uint8_t* gp, int lane, bool act
 // One LDS round of the column fit: KG candidates c = binary16(gamma * c0), the
 // impact-weighted error F = c^2 sum_i (sqrt(w_i) r_i)^2 (t_ij / c - Q_ij)^2 of the
 // wave's rows, combined over the waves; the best candidate so far is kept (strict <).
+// part[] is read by every wave after the barrier: a later round must synchronize first.
 template <class Sh, int KG, bool FREE0, class Smem>
 __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float* c0, const float* grid, int g0,
                                            int n_grid, int wave, int lane, bool act, float* cbest, float* fbest) {
@@ -381,7 +395,6 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
             }
         }
     }
-    __syncthreads();
 }
 
 template <int DK, int DV, int MODE, int KG>
@@ -435,10 +448,10 @@ k_state(StepParams a) {
         for (int c = 0; c < CPL; ++c) c_old[c] = act ? h2f(rs[DK + col0 + c]) : 1.f;
     }
 
-    // ---- phase 0: per-row coefficients (one thread per storage row)
+    // ---- phase 0: per-row coefficients of this wave's rows (lane r < RPW takes row wave * RPW + r)
     float kq_part = 0.f, kb_part = 0.f, qb_part = 0.f;
-    if (tid < DK) {
-        const int t = tid;
+    if (lane < RPW) {
+        const int t = wave * RPW + lane;
         const int rbits = a.t.row_bits[(size_t)lh * DK + t];
         const int sb = gbits[t / GR];
         const bool piv = rbits == 16;
@@ -473,7 +486,7 @@ k_state(StepParams a) {
             sm.red[wave][2] = qb_part;
         }
     }
-    __syncthreads();
+    wave_lds_sync();
 
     float X[EPL];
 
@@ -653,7 +666,7 @@ k_state(StepParams a) {
             sm.fin[t] = make_float2(mb - qmax, mb + qmax);
         }
     }
-    __syncthreads();
+    wave_lds_sync();
 
     // ---- phase 4: t = X / r_i (code rows; pivot rows have r = 1) and the column base
     float c0[CPL];
@@ -691,17 +704,16 @@ k_state(StepParams a) {
         }
         if (act) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) sm.part[wave][0][col0 + c] = c0p[c];
+            for (int c = 0; c < CPL; ++c) sm.cmax[wave][col0 + c] = c0p[c];
         }
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             float m = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) m = fmaxf(m, act ? sm.part[w][0][col0 + c] : 0.f);
+            for (int w = 0; w < NW; ++w) m = fmaxf(m, act ? sm.cmax[w][col0 + c] : 0.f);
             c0[c] = m;
         }
-        __syncthreads();   // part[] is reused below
     }
 
     // ---- phase 5: column fit over the candidate grid, KG candidates per LDS round
@@ -717,8 +729,10 @@ k_state(StepParams a) {
         // so the first round skips the clamp of its first candidate when grid[0] == 1
         if (a.unit_first) grid_round<Sh, KG, true>(sm, X, c0, a.grid, 0, n_grid, wave, lane, act, cbest, fbest);
         else grid_round<Sh, KG, false>(sm, X, c0, a.grid, 0, n_grid, wave, lane, act, cbest, fbest);
-        for (int g0 = KG; g0 < n_grid; g0 += KG)
+        for (int g0 = KG; g0 < n_grid; g0 += KG) {
+            __syncthreads();   // every wave has read the previous round's partials
             grid_round<Sh, KG, false>(sm, X, c0, a.grid, g0, n_grid, wave, lane, act, cbest, fbest);
+        }
     }
     float ic[CPL];
 #pragma unroll
@@ -761,7 +775,7 @@ k_state(StepParams a) {
             if (act) store_dw<8>(gp + lane * 32, d);
         }
     }
-    if (tid < DK) rs[tid] = (uint16_t)f2h_bits(sm.rn[tid]);
+    if (lane < RPW) rs[wave * RPW + lane] = (uint16_t)f2h_bits(sm.rn[wave * RPW + lane]);
     if (wave == 0 && act) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) rs[DK + col0 + c] = (uint16_t)f2h_bits(cbest[c]);
