@@ -39,7 +39,9 @@ def parse():
     ap.add_argument("--split", action="store_true", help="time the two-stream arrangement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--extras", action="store_true", help="also time the 4-bit pool and the copy reference")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the comparators (INT8 per-row, FP32), the split arrangement, the candidate-grid "
+                         "sweep, the 4-bit budget and the copy reference")
     return ap.parse_args()
 
 
@@ -60,6 +62,26 @@ def algorithmic_bytes(plan, batch, sq):
     return int(batch * (2 * state_bytes.sum() + L * H * io))
 
 
+def per_state_bytes(dk, dv, form, state_bytes):
+    gate = 4 * (dk if form == 1 else 1)
+    return 2 * state_bytes + 4 * (2 * dk + 2 * dv + 1) + gate
+
+
+def time_calls(fn, n, warm=2):
+    """Mean milliseconds per call over n calls on torch's current stream (HIP events)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def traffic_per_launch():
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -78,35 +100,57 @@ def traffic_per_launch():
         return None
 
 
-def cpu_baseline(wl, seconds, seed=7):
-    """The float64 oracle on a sample of the workload's states, timed on the host."""
+def _oracle_sample(wl, seed, n=64):
+    """A seeded sample of the workload's states (6-bit rows, oracle-quantized) and one step's inputs."""
     import numpy as np
     from oracle import quant
-    from oracle.step import packed_step
     from workloads import gen
 
     g = np.random.default_rng(seed)
-    n = 64
     gates = gen.unit_gates(wl)
     imp = gen.impact_scores(wl)
     lh = g.integers(0, wl.n_layers * wl.n_heads, size=n)
     alpha = gates.reshape(-1)[lh].astype(np.float64)
     w = imp.reshape(-1, wl.d_k)[lh].astype(np.float64)
     rows = quant.RowPlan(bits=np.full((n, wl.d_k), 6), pivot=np.zeros((n, wl.d_k), bool), w=w)
-    X = g.standard_normal((n, wl.d_k, wl.d_v))
-    P = quant.quantize(X, rows, wl.grid)
+    P = quant.quantize(g.standard_normal((n, wl.d_k, wl.d_v)), rows, wl.grid)
     q, k, v, beta = [a[0, 0, 0] for a in gen.eval_inputs(wl.scaled(n_layers=1, n_heads=n), 1, 1, 1)]
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        P, _, _ = packed_step(P, rows, q, k, v, alpha, beta, wl.grid)
-        done += n
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": done / el, "unit": "state-updates/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} state updates ({n} sampled (layer, head) states of the workload, 6-bit rows, "
-                      f"steps repeated for {el:.1f} s) by the float64 NumPy oracle in one host thread"}
+    return P, rows, q, k, v, alpha, beta
+
+
+def _oracle_run(args):
+    """Oracle steps over the sample until `seconds` have passed; returns (state updates, elapsed s)."""
+    wl_name, seed, seconds = args
+    from threadpoolctl import threadpool_limits
+    from oracle.step import packed_step
+    from workloads import configs
+    wl = configs.BY_NAME[wl_name]
+    P, rows, q, k, v, alpha, beta = _oracle_sample(wl, seed)
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            P, _, _ = packed_step(P, rows, q, k, v, alpha, beta, wl.grid)
+            done += P.Q.shape[0]
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return done, el
+
+
+def cpu_baseline(wl, seconds):
+    """The float64 oracle on a bounded sample of the workload's states, timed on the host: one thread for a
+    third of the time, then one process per available core (at most 16) for the rest."""
+    import multiprocessing as mp
+    n1, t1 = _oracle_run((wl.name, 7, seconds / 3))
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    with mp.get_context("fork").Pool(cores) as pool:
+        res = pool.map(_oracle_run, [(wl.name, 100 + i, 2 * seconds / 3) for i in range(cores)])
+    done = sum(r[0] for r in res)
+    wall = max(r[1] for r in res)
+    return {"value": done / wall, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
+            "single_thread": n1 / t1,
+            "sample": f"{done} state updates over {cores} processes (each 64 sampled (layer, head) states of the "
+                      f"workload with 6-bit rows, steps repeated for {2 * seconds / 3:.0f} s) plus {n1} in one "
+                      f"thread, by the float64 NumPy oracle, BLAS limited to one thread per process"}
 
 
 def main():
@@ -116,12 +160,16 @@ def main():
               f"and each GPU's share is the single-GPU workload", file=sys.stderr)
         sys.exit(2)
     import numpy as np
-    import torch
-
-    import quantized_delta_rule_02_amd as sq
     from workloads import configs, gen
 
     wl = configs.BY_NAME[args.workload]
+    # the oracle runs first, in forked host processes, before anything initializes the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_seconds)
+    if cpu is not None:
+        log(f"cpu baseline: {cpu['value']:.0f} state-updates/s on {cpu['cores']} cores")
+    import torch
+
+    import quantized_delta_rule_02_amd as sq
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L, H, dk, dv, B = wl.n_layers, wl.n_heads, wl.d_k, wl.d_v, wl.batch
@@ -167,11 +215,34 @@ def main():
         sq.sq_fp32_step(form, H, dk, dv, B, 0, L, B, ident, S, q, k, v, gate, beta, y)
     sq.sq_pack(pool, 0, L, B, slots, S)
     torch.cuda.synchronize()
-    del S
-    torch.cuda.empty_cache()
     log(f"state warm-up ({args.state_warmup} fp32 steps) + pack: {time.perf_counter() - t0:.1f} s")
 
     batches = [inputs(s) for s in (1, 2)]
+    extras = {}
+    if not args.no_extras:
+        # the same update on other state formats, same inputs: float32 states and uniform INT8 per-row states
+        q1, k1, v1, b1 = batches[0]
+        ms32 = time_calls(lambda: sq.sq_fp32_step(form, H, dk, dv, B, 0, L, B, ident, S, q1, k1, v1, gate, b1, y),
+                          args.steps)
+        by32 = per_state_bytes(dk, dv, form, 4 * dk * dv)
+        extras["fp32_step"] = {"ms": ms32, "state_updates_per_s": n_states / (ms32 / 1e3),
+                               "GBps": n_states * by32 / (ms32 / 1e3) / 1e9, "state_bytes": 4 * dk * dv}
+        codes8 = torch.empty(n_states * dk * dv, dtype=torch.int8, device=dev)
+        scales8 = torch.empty(n_states * dk, dtype=torch.float32, device=dev)
+        Sv, Cv, Rv = S.view(n_states, dk, dv), codes8.view(n_states, dk, dv), scales8.view(n_states, dk)
+        for i0 in range(0, n_states, 8192):
+            blk = Sv[i0:i0 + 8192]
+            sc = (blk.abs().amax(dim=2) / 127.0).clamp_min(1e-30)
+            Rv[i0:i0 + 8192] = sc
+            Cv[i0:i0 + 8192] = torch.clamp(torch.round(blk / sc[:, :, None]), -127, 127).to(torch.int8)
+        ms8 = time_calls(lambda: sq.sq_int8_step(form, H, dk, dv, B, 0, L, B, ident, codes8, scales8, q1, k1, v1,
+                                                 gate, b1, y), args.steps)
+        by8 = per_state_bytes(dk, dv, form, dk * dv + 4 * dk)
+        extras["int8_step"] = {"ms": ms8, "state_updates_per_s": n_states / (ms8 / 1e3),
+                               "GBps": n_states * by8 / (ms8 / 1e3) / 1e9, "state_bytes": dk * dv + 4 * dk}
+        del codes8, scales8, Sv, Cv, Rv
+    del S
+    torch.cuda.empty_cache()
     aux = torch.cuda.Stream() if args.split else None
     flags = sq.SQ_STEP_SPLIT if args.split else 0
 
@@ -226,7 +297,49 @@ def main():
                      "launch_ms": ms},
         "wall_s_timed": wall,
     }
-    if args.extras:
+    if not args.no_extras:
+        q1, k1, v1, b1 = batches[0]
+        # two-stream arrangement: readout kernel on the main stream, fit + pack on a second stream
+        aux2 = torch.cuda.Stream()
+        mss = time_calls(lambda: sq.sq_state_step(pool, 0, L, B, slots, q1, k1, v1, gate, b1, y, stream_aux=aux2,
+                                                  flags=sq.SQ_STEP_SPLIT), args.steps)
+        extras["split2"] = {"ms": mss, "state_updates_per_s": per_step / (mss / 1e3)}
+        # candidate-grid sweep on the same packed pool (the grid does not change the layout)
+        units = sq.sq_plan_units(plan)["unit_bits"]
+        sweep = {}
+        grids = {1: (1.0,), 2: (1.0, 0.875), 4: tuple(wl.grid),
+                 8: (1.0, 0.9375, 0.875, 0.8125, 0.75, 0.6875, 0.625, 0.5625)}
+        for G, grid in grids.items():
+            if G == len(wl.grid):
+                sweep[str(G)] = ms
+                continue
+            pg = sq.sq_plan_create(form=form, unit=unit, n_layers=L, n_heads=H, d_k=dk, d_v=dv, widths=wl.widths,
+                                   budget_milli=wl.budget_milli, pivot_ppm=wl.pivot_ppm, grid=grid,
+                                   gate=gen.unit_gates(wl), impact=gen.impact_scores(wl), unit_bits=units)
+            poolg = sq.sq_pool_create(pg, pool_mem, wl.n_slots)
+            sweep[str(G)] = time_calls(lambda: sq.sq_state_step(poolg, 0, L, B, slots, q1, k1, v1, gate, b1, y),
+                                       args.steps)
+            poolg.close()
+            pg.close()
+        extras["grid_sweep_ms"] = sweep
+        # 4.0-bit budget: with widths {4, 6, 8} every non-pivot unit takes 4 bits; same pivots
+        p4 = sq.sq_plan_create(form=form, unit=unit, n_layers=L, n_heads=H, d_k=dk, d_v=dv, widths=wl.widths,
+                               budget_milli=4000, pivot_ppm=wl.pivot_ppm, grid=wl.grid, gate=gen.unit_gates(wl),
+                               impact=gen.impact_scores(wl), unit_bits=np.where(units == 16, 16, 4).astype(np.int32))
+        mem4 = torch.empty(sq.sq_pool_bytes(p4, wl.n_slots), dtype=torch.uint8, device=dev)
+        pool4 = sq.sq_pool_create(p4, mem4, wl.n_slots)
+        Xr = torch.randn(B * H * dk * dv, device=dev)
+        for layer in range(L):
+            sq.sq_pack(pool4, layer, 1, B, slots, Xr)
+        del Xr
+        ms4 = time_calls(lambda: sq.sq_state_step(pool4, 0, L, B, slots, q1, k1, v1, gate, b1, y), args.steps)
+        alg4 = algorithmic_bytes(p4, B, sq)
+        extras["budget_4bit"] = {"ms": ms4, "state_updates_per_s": per_step / (ms4 / 1e3),
+                                 "GBps": alg4 / (ms4 / 1e3) / 1e9, "algorithmic_bytes_per_launch": alg4,
+                                 "compression_vs_fp32": round(p4.desc["compression_vs_fp32"], 4)}
+        pool4.close()
+        p4.close()
+        del mem4
         src = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         sq.sq_copy(src, dst)
@@ -237,10 +350,12 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         cms = ev0.elapsed_time(ev1) / 5
-        out["copy_reference"] = {"bytes_moved": 2 * src.numel(), "ms": cms, "GBps": 2 * src.numel() / cms / 1e6}
+        extras["copy_reference"] = {"bytes_moved": 2 * src.numel(), "ms": cms,
+                                    "GBps": 2 * src.numel() / cms / 1e6}
         del src, dst
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        out["extras"] = extras
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     pool.close()
     plan.close()

@@ -879,6 +879,43 @@ struct CmpParams {
 
 // Uniform INT8 per-row state and the unquantized FP32 state: same wave/lane
 // mapping as the packed step, row-major state storage.
+// A lane's CPL adjacent entries of one row (CPL = 1, 2 or 4; the offset of the first is a
+// multiple of CPL, so the access is naturally aligned).
+template <int CPL>
+__device__ __forceinline__ void cmp_load_i8(const int8_t* p, bool act, float* x) {
+    uint32_t v = 0;
+    if (act) {
+        if constexpr (CPL == 1) v = (uint8_t)*p;
+        else if constexpr (CPL == 2) v = *reinterpret_cast<const uint16_t*>(p);
+        else v = *reinterpret_cast<const uint32_t*>(p);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) x[c] = (float)(int8_t)(v >> (8 * c));
+}
+template <int CPL>
+__device__ __forceinline__ void cmp_store_i8(int8_t* p, uint32_t v) {
+    if constexpr (CPL == 1) *p = (int8_t)v;
+    else if constexpr (CPL == 2) *reinterpret_cast<uint16_t*>(p) = (uint16_t)v;
+    else *reinterpret_cast<uint32_t*>(p) = v;
+}
+template <int CPL>
+__device__ __forceinline__ void cmp_load_f32(const float* p, bool act, float* x) {
+    if constexpr (CPL == 1) x[0] = act ? *p : 0.f;
+    else if constexpr (CPL == 2) {
+        const float2 v = act ? *reinterpret_cast<const float2*>(p) : make_float2(0.f, 0.f);
+        x[0] = v.x; x[1] = v.y;
+    } else {
+        const float4 v = act ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    }
+}
+template <int CPL>
+__device__ __forceinline__ void cmp_store_f32(float* p, const float* x) {
+    if constexpr (CPL == 1) *p = x[0];
+    else if constexpr (CPL == 2) *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+    else *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
 template <int DK, int DV, bool INT8>
 __global__ void __launch_bounds__(nw_of(DK, DV) * 64)
 k_cmp(CmpParams a) {
@@ -917,16 +954,13 @@ k_cmp(CmpParams a) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
         const int t = wave * RPW + r;
+        // the lane's CPL adjacent entries of the row in one access
+        if constexpr (INT8) cmp_load_i8<CPL>(a.codes + (st * DK + t) * DV + col0, act, &X[r * CPL]);
+        else cmp_load_f32<CPL>(a.S + (st * DK + t) * DV + col0, act, &X[r * CPL]);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            float x = 0.f;
-            if (act) {
-                if constexpr (INT8) x = (float)a.codes[(st * DK + t) * DV + col0 + c];
-                else x = a.S[(st * DK + t) * DV + col0 + c];
-            }
-            X[r * CPL + c] = x;
-            U[c] = fmaf(s_ck[t], x, U[c]);
-            P[c] = fmaf(s_cq[t], x, P[c]);
+            U[c] = fmaf(s_ck[t], X[r * CPL + c], U[c]);
+            P[c] = fmaf(s_cq[t], X[r * CPL + c], P[c]);
         }
     }
     if (act) {
@@ -965,9 +999,7 @@ k_cmp(CmpParams a) {
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
             const int t = wave * RPW + r;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                if (act) a.S[(st * DK + t) * DV + col0 + c] = X[r * CPL + c];
+            if (act) cmp_store_f32<CPL>(a.S + (st * DK + t) * DV + col0, &X[r * CPL]);
         }
         return;
     } else {
@@ -984,19 +1016,21 @@ k_cmp(CmpParams a) {
         if (act && (lane & (LPR / RPW - 1)) == 0) {
             const int t = wave * RPW + row;
             const float s = rm[0] > 0.f ? rm[0] / 127.f : 1.f;
-            s_sc[t] = s;
+            s_sc[t] = 1.f / s;   // one division per row, by the lane that holds the row maximum
             a.scales[st * DK + t] = s;
         }
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
             const int t = wave * RPW + r;
-            const float inv = 1.f / s_sc[t];
+            const float inv = s_sc[t];
+            uint32_t packed = 0;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const float qv = med3(rintf(X[r * CPL + c] * inv), -127.f, 127.f);
-                if (act) a.codes[(st * DK + t) * DV + col0 + c] = (int8_t)(int)qv;
+                packed |= ((uint32_t)(int)qv & 0xFFu) << (8 * c);
             }
+            if (act) cmp_store_i8<CPL>(a.codes + (st * DK + t) * DV + col0, packed);
         }
     }
 }
