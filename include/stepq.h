@@ -56,6 +56,8 @@ typedef int32_t sq_status;
 #define SQ_FORM_KDA 1             /* one retention gate per key row: D = diag(alpha) */
 #define SQ_UNIT_HEAD 0            /* allocation unit: a whole head state             */
 #define SQ_UNIT_ROW  1            /* allocation unit: one key row of a head state    */
+#define SQ_QUANT_DUAL_AXIS 0      /* row factors sqrt(m / w) + impact-weighted column fit (the method) */
+#define SQ_QUANT_ROW_ABSMAX 1     /* per-row absmax r = m / qmax, column scales 1 (ablation: no fit) */
 
 #define SQ_MAX_WIDTHS 4
 #define SQ_MAX_GRID   8
@@ -84,6 +86,8 @@ typedef struct sq_plan_cfg {
     int32_t calib_segments;       /* S */
     int32_t calib_len;            /* T */
     int32_t n_threads;            /* planner threads; 0 = all hardware threads */
+    int32_t quantizer;            /* SQ_QUANT_DUAL_AXIS (0) or SQ_QUANT_ROW_ABSMAX (1; rcap.io post, the
+                                     ablation paragraph: the allocation without the dual-axis fit) */
 } sq_plan_cfg;
 
 typedef struct sq_plan sq_plan;   /* host-side plan (opaque) */
@@ -99,6 +103,7 @@ typedef struct sq_plan_desc {
     double code_bits_per_entry;   /* allocated bits per state entry, pivots at 16, scales excluded */
     double stored_bits_per_entry; /* slot_bytes * 8 / (L * H * d_k * d_v): codes + scales + padding */
     double compression_vs_fp32;   /* 32 / stored_bits_per_entry */
+    int32_t quantizer;            /* SQ_QUANT_* */
 } sq_plan_desc;
 
 /* ---- plan (CPU) --------------------------------------------------------
@@ -140,6 +145,7 @@ void      sq_pool_destroy(sq_pool* pool);
 
 #define SQ_STEP_SPLIT    1u       /* two kernels: readout on stream_main, fit + pack on stream_aux */
 #define SQ_STEP_VALIDATE 2u       /* copy the slot list to the host and check range and uniqueness */
+#define SQ_STEP_NO_JOIN  4u       /* with SQ_STEP_SPLIT: return without making stream_main wait for stream_aux */
 
 /* ---- state_step --------------------------------------------------------
  * One decode step for batch requests over layers [layer0, layer0 + n_layers)
@@ -154,7 +160,14 @@ void      sq_pool_destroy(sq_pool* pool);
  * Slots must be distinct within a call (otherwise the result is undefined;
  * SQ_STEP_VALIDATE checks it and returns SQ_ERR_SLOT).  Enqueued on
  * stream_main (and stream_aux with SQ_STEP_SPLIT; ordered by events, the call
- * returns with stream_main waiting for all of its work). */
+ * returns with stream_main waiting for all of its work).
+ * SQ_STEP_SPLIT | SQ_STEP_NO_JOIN leaves the fit + pack of the call running on
+ * stream_aux so that later work on stream_main (another layer's readout, the
+ * model's own kernels) overlaps it (hyper.ai summary, 方法, the second-stream
+ * arrangement).  The caller then orders anything that touches the same layers
+ * (the next step's call for them, sq_export, ...) after stream_aux; calls for
+ * other layers may follow on stream_main at once.  The split scratch holds one
+ * region per (layer, slot index < n_slots), so such calls do not share it. */
 sq_status sq_state_step(sq_pool* pool, int32_t layer0, int32_t n_layers, int32_t batch,
                         const int32_t* d_slots, const float* d_q, const float* d_k,
                         const float* d_v, const float* d_gate, const float* d_beta, float* d_y,

@@ -27,7 +27,8 @@ Readings taken
 * distortion D_u(b) = mean over calibration snapshots (the state at the end of
   each segment, unquantized recurrence from zero) of the summed squared error
   of the unit's entries when the whole state is quantized by the dual-axis
-  quantizer with every row at width b and no pivots.
+  quantizer with every row at width b and no pivots (the plan's quantizer:
+  dual-axis, or per-row absmax for the ablation of the fit).
 * pivots: ceil(ppm * U / 1e6) units ranked by L desc, then D(smallest width)
   desc, then unit index asc.  Pivots sit outside the budget.
 * allocation: exact dynamic programme over the non-pivot units in index order,
@@ -84,14 +85,14 @@ def calib_snapshots(q, k, v, beta, alpha_head) -> np.ndarray:
     return S
 
 
-def head_distortion(snap, w_head, widths, grid, unit: str) -> np.ndarray:
-    """D(b) for the units of one head: [1, nb] (head unit) or [d_k, nb] (row units)."""
+def head_distortion(snap, w_head, widths, grid, unit: str, mode: str = "dual_axis") -> np.ndarray:
+    """D(b) for the units of one head: [1, nb] (head unit) or [d_k, nb] (row units), with the plan's quantizer."""
     n_seg, d_k, _ = snap.shape
     out = []
     for b in widths:
         rows = quant.RowPlan(bits=np.full((n_seg, d_k), b), pivot=np.zeros((n_seg, d_k), bool),
                              w=np.broadcast_to(np.asarray(w_head, np.float64), (n_seg, d_k)))
-        P = quant.quantize(snap, rows, grid)
+        P = quant.quantize(snap, rows, grid, mode=mode)
         err = snap - quant.dequantize(P, rows)
         e2 = np.sum(err * err, axis=2)            # [S, d_k] per-row squared error
         out.append(e2.sum(axis=1).mean()[None] if unit == HEAD else e2.mean(axis=0))
@@ -180,8 +181,9 @@ class Plan:
 
 def make_plan(form: str, unit: str, n_layers: int, n_heads: int, d_k: int, d_v: int,
               widths, budget_milli: int, pivot_ppm: int, grid, alpha_unit,
-              traces: Callable, impact=None) -> Plan:
-    """Full planner.  traces(l, h) -> (q, k, v, beta) arrays of shape [S, T, ...]."""
+              traces: Callable, impact=None, mode: str = "dual_axis") -> Plan:
+    """Full planner.  traces(l, h) -> (q, k, v, beta) arrays of shape [S, T, ...]; mode = the quantizer
+    whose distortion the allocation weighs (quant.MODES)."""
     widths = tuple(sorted(widths))
     lbar = unit_log_retention(alpha_unit, form, unit, d_k)
     L = lifetime_weight(lbar)
@@ -199,7 +201,7 @@ def make_plan(form: str, unit: str, n_layers: int, n_heads: int, d_k: int, d_v: 
                 w_all[l, h] = impact[l, h]
             snap = calib_snapshots(q, k, v, beta, a_h)
             u0 = (l * n_heads + h) * per
-            D[u0:u0 + per] = head_distortion(snap, w_all[l, h], widths, grid, unit)
+            D[u0:u0 + per] = head_distortion(snap, w_all[l, h], widths, grid, unit, mode)
     piv = select_pivots(L, D[:, 0], pivot_count(pivot_ppm, U))
     is_piv = np.zeros(U, bool)
     is_piv[piv] = True

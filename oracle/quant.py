@@ -34,6 +34,13 @@ Readings taken where the pages are open
   gets c = 1 and zero codes.
 * pivot rows are stored as binary16 values of X (saturating) and take no part
   in the row factors, the column base or the fit.
+
+Second quantizer, for the ablations (rcap.io post, the paragraph on the
+ablation: temporal allocation alone, i.e. the allocation and pivots with a
+plain quantizer instead of the dual-axis fit): symmetric per-row absmax,
+r_i = binary16(m_i / qmax_i), every column scale 1, the same rounding and
+clamp.  Reading: "plain" is the per-row absmax scale of the uniform baseline,
+with the scale stored in binary16 like the dual-axis factors.
 """
 from __future__ import annotations
 
@@ -136,9 +143,41 @@ class QuantDiag:
     z: np.ndarray         # [N, d_k, d_v] pre-rounding code values with the chosen scales
 
 
-def quantize(X, rows: RowPlan, grid, scale_fp16: bool = True, diag: bool = False):
-    """Dual-axis quantization of float states X [N, d_k, d_v].  Returns Packed (and QuantDiag)."""
+MODES = ("dual_axis", "row_absmax")
+
+
+def row_absmax_factors(X, rows: RowPlan, scale_fp16: bool = True):
+    """Per-row absmax factors r_i = m_i / qmax_i.  Returns (r_pre, r_stored); zero and pivot rows get 1."""
+    m = np.max(np.abs(X), axis=2)
+    r_pre = m / rows.qmax
+    r = _scale_round(r_pre, scale_fp16)
+    r = np.where(m > 0, r, 1.0)
+    r = np.where(rows.pivot, 1.0, r)
+    return r_pre, r
+
+
+def _quantize_row_absmax(X, rows: RowPlan, scale_fp16: bool, diag: bool):
+    N, d_k, d_v = X.shape
+    r_pre, r = row_absmax_factors(X, rows, scale_fp16)
+    c = np.ones((N, d_v))
+    Q, z = codes_for(X, rows, r, c)
+    piv = np.asarray(rows.pivot)[:, :, None]
+    V = np.where(piv, fp16_round(X) if scale_fp16 else X, 0.0)
+    P = Packed(Q=Q.astype(np.int64), r=r, c=c, V=V)
+    if not diag:
+        return P
+    F = fit_objective(X, rows, r, c, Q)[None]
+    return P, QuantDiag(r_pre=r_pre, c0=c, cands=c[None], F=F, g=np.zeros((N, d_v), np.int64), z=z)
+
+
+def quantize(X, rows: RowPlan, grid, scale_fp16: bool = True, diag: bool = False, mode: str = "dual_axis"):
+    """Quantization of float states X [N, d_k, d_v] (dual-axis fit, or per-row absmax when
+    mode == "row_absmax", which ignores the grid).  Returns Packed (and QuantDiag)."""
     X = np.asarray(X, dtype=np.float64)
+    if mode == "row_absmax":
+        return _quantize_row_absmax(X, rows, scale_fp16, diag)
+    if mode != "dual_axis":
+        raise ValueError(f"unknown quantizer {mode!r}")
     N, d_k, d_v = X.shape
     r_pre, r = row_factors(X, rows, scale_fp16)
     c0 = column_base(X, rows, r)

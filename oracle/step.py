@@ -17,11 +17,12 @@ from .recurrence import delta_update
 
 
 def packed_step(P: quant.Packed, rows: quant.RowPlan, q, k, v, alpha, beta, grid,
-                scale_fp16: bool = True, diag: bool = False):
-    """Returns (Packed', y [N, d_v], X [N, d_k, d_v]) and the quantizer diagnostics if diag."""
+                scale_fp16: bool = True, diag: bool = False, mode: str = "dual_axis"):
+    """Returns (Packed', y [N, d_v], X [N, d_k, d_v]) and the quantizer diagnostics if diag;
+    mode selects the quantizer (quant.MODES)."""
     S = quant.dequantize(P, rows)
     X, y = delta_update(S, q, k, v, alpha, beta)
-    out = quant.quantize(X, rows, grid, scale_fp16=scale_fp16, diag=diag)
+    out = quant.quantize(X, rows, grid, scale_fp16=scale_fp16, diag=diag, mode=mode)
     if diag:
         P2, D = out
         return P2, y, X, D

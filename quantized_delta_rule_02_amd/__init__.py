@@ -14,15 +14,15 @@ from ctypes import POINTER, byref, c_double, c_float, c_int32, c_size_t, c_void_
 import numpy as np
 
 from . import _lib
-from ._lib import (SQ_FORM_GDN, SQ_FORM_KDA, SQ_PIVOT_BITS, SQ_STEP_SPLIT, SQ_STEP_VALIDATE, SQ_UNIT_HEAD,
-                   SQ_UNIT_ROW)
+from ._lib import (SQ_FORM_GDN, SQ_FORM_KDA, SQ_PIVOT_BITS, SQ_QUANT_DUAL_AXIS, SQ_QUANT_ROW_ABSMAX,
+                   SQ_STEP_NO_JOIN, SQ_STEP_SPLIT, SQ_STEP_VALIDATE, SQ_UNIT_HEAD, SQ_UNIT_ROW)
 
 __all__ = [
     "StepQError", "Plan", "Pool", "sq_plan_create", "sq_plan_describe", "sq_plan_units", "sq_plan_rows",
     "sq_plan_save", "sq_plan_load", "sq_calib_generate", "sq_pool_bytes", "sq_pool_create", "sq_state_step",
     "sq_pack", "sq_unpack", "sq_export", "sq_import", "sq_int8_step", "sq_fp32_step", "sq_copy",
     "sq_supported_shapes", "SQ_FORM_GDN", "SQ_FORM_KDA", "SQ_UNIT_HEAD", "SQ_UNIT_ROW", "SQ_STEP_SPLIT",
-    "SQ_STEP_VALIDATE", "SQ_PIVOT_BITS",
+    "SQ_STEP_VALIDATE", "SQ_STEP_NO_JOIN", "SQ_PIVOT_BITS", "SQ_QUANT_DUAL_AXIS", "SQ_QUANT_ROW_ABSMAX",
 ]
 
 
@@ -69,7 +69,7 @@ class Plan:
 
 def sq_plan_create(*, form, unit, n_layers, n_heads, d_k, d_v, widths, budget_milli, pivot_ppm, grid, gate,
                    impact=None, unit_bits=None, calib=None, calib_seed=0, calib_segments=32, calib_len=512,
-                   n_threads=0) -> Plan:
+                   n_threads=0, quantizer=SQ_QUANT_DUAL_AXIS) -> Plan:
     """Run the offline planner.  gate/impact/unit_bits/calib are host arrays (calib = (q, k, v, beta))."""
     lib = _lib.load()
     cfg = _lib.SqPlanCfg()
@@ -121,6 +121,7 @@ def sq_plan_create(*, form, unit, n_layers, n_heads, d_k, d_v, widths, budget_mi
         cfg.calib_beta = arrs[3].ctypes.data_as(POINTER(c_float))
     cfg.calib_seed = int(calib_seed)
     cfg.calib_segments, cfg.calib_len, cfg.n_threads = int(calib_segments), int(calib_len), int(n_threads)
+    cfg.quantizer = int(quantizer)
     out = c_void_p()
     _check(lib.sq_plan_create(byref(cfg), byref(out)), "sq_plan_create")
     return Plan(out.value)

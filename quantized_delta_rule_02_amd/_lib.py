@@ -13,7 +13,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "stepq.h")
 SQ_OK = 0
 SQ_FORM_GDN, SQ_FORM_KDA = 0, 1
 SQ_UNIT_HEAD, SQ_UNIT_ROW = 0, 1
-SQ_STEP_SPLIT, SQ_STEP_VALIDATE = 1, 2
+SQ_QUANT_DUAL_AXIS, SQ_QUANT_ROW_ABSMAX = 0, 1
+SQ_STEP_SPLIT, SQ_STEP_VALIDATE, SQ_STEP_NO_JOIN = 1, 2, 4
 SQ_PIVOT_BITS = 16
 SQ_MAX_WIDTHS, SQ_MAX_GRID = 4, 8
 
@@ -30,6 +31,7 @@ class SqPlanCfg(ctypes.Structure):
         ("calib_v", POINTER(c_float)), ("calib_beta", POINTER(c_float)),
         ("calib_seed", c_uint64), ("calib_segments", c_int32), ("calib_len", c_int32),
         ("n_threads", c_int32),
+        ("quantizer", c_int32),
     ]
 
 
@@ -41,6 +43,7 @@ class SqPlanDesc(ctypes.Structure):
         ("slot_bytes", c_uint64),
         ("code_bits_per_entry", c_double), ("stored_bits_per_entry", c_double),
         ("compression_vs_fp32", c_double),
+        ("quantizer", c_int32),
     ]
 
 

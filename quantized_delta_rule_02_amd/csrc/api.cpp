@@ -42,7 +42,7 @@ using namespace sq;
 
 struct sq_pool {
     uint64_t plan_id;
-    int32_t L, H, dk, dv, form, n_slots, n_grid;
+    int32_t L, H, dk, dv, form, n_slots, n_grid, quantizer;
     float grid[kMaxGrid];
     uint8_t* pool;
     size_t pool_bytes;
@@ -99,6 +99,10 @@ static sq_status validate_cfg(const sq_plan_cfg* c) {
             if (c->widths[j] == b) { set_error("width %d repeated", b); return SQ_ERR_ARG; }
     }
     if (c->pivot_ppm < 0 || c->pivot_ppm > 1000000) { set_error("pivot_ppm %d", c->pivot_ppm); return SQ_ERR_ARG; }
+    if (c->quantizer != SQ_QUANT_DUAL_AXIS && c->quantizer != SQ_QUANT_ROW_ABSMAX) {
+        set_error("quantizer %d", c->quantizer);
+        return SQ_ERR_ARG;
+    }
     if (c->n_grid < 1 || c->n_grid > SQ_MAX_GRID) { set_error("n_grid %d not in 1..%d", c->n_grid, SQ_MAX_GRID); return SQ_ERR_UNSUPPORTED; }
     for (int g = 0; g < c->n_grid; ++g)
         if (!(c->grid[g] > 0.f) || !std::isfinite(c->grid[g])) { set_error("grid[%d] not positive", g); return SQ_ERR_ARG; }
@@ -126,6 +130,7 @@ extern "C" sq_status sq_plan_create(const sq_plan_cfg* cfg, sq_plan** out) {
     p->widths.assign(cfg->widths, cfg->widths + cfg->n_widths);
     std::sort(p->widths.begin(), p->widths.end());
     p->budget_milli = cfg->budget_milli; p->pivot_ppm = cfg->pivot_ppm;
+    p->quantizer = cfg->quantizer;
     p->grid.assign(cfg->grid, cfg->grid + cfg->n_grid);
     try {
         st = run_planner(*cfg, *p);
@@ -157,6 +162,7 @@ extern "C" sq_status sq_plan_describe(const sq_plan* p, sq_plan_desc* out) {
     out->code_bits_per_entry = bits / entries;
     out->stored_bits_per_entry = double(p->slot_bytes) * 8.0 / entries;
     out->compression_vs_fp32 = 32.0 / out->stored_bits_per_entry;
+    out->quantizer = p->quantizer;
     return SQ_OK;
 }
 
@@ -210,13 +216,13 @@ struct Reader {
         i += m * sizeof(T);
     }
 };
-const char kMagic[8] = {'S', 'Q', 'P', 'L', 'A', 'N', '0', '1'};
+const char kMagic[8] = {'S', 'Q', 'P', 'L', 'A', 'N', '0', '2'};
 }  // namespace
 
 static void serialize(const sq_plan& p, Writer& w) {
     for (char c : kMagic) w.put(c);
     w.put(p.form); w.put(p.unit); w.put(p.L); w.put(p.H); w.put(p.dk); w.put(p.dv);
-    w.put(p.budget_milli); w.put(p.pivot_ppm);
+    w.put(p.budget_milli); w.put(p.pivot_ppm); w.put(p.quantizer);
     w.vec(p.widths); w.vec(p.grid);
     w.vec(p.lbar); w.vec(p.lifetime); w.vec(p.distortion); w.vec(p.unit_bits); w.vec(p.row_bits); w.vec(p.impact);
 }
@@ -242,7 +248,9 @@ extern "C" sq_status sq_plan_load(const void* buf, size_t bytes, sq_plan** out) 
     if (!p) { set_error("host allocation"); return SQ_ERR_NOMEM; }
     p->form = r.get<int32_t>(); p->unit = r.get<int32_t>(); p->L = r.get<int32_t>(); p->H = r.get<int32_t>();
     p->dk = r.get<int32_t>(); p->dv = r.get<int32_t>(); p->budget_milli = r.get<int32_t>(); p->pivot_ppm = r.get<int32_t>();
+    p->quantizer = r.get<int32_t>();
     bool ok = r.ok && (p->form == 0 || p->form == 1) && (p->unit == 0 || p->unit == 1) && p->L >= 1 && p->H >= 1 &&
+              (p->quantizer == SQ_QUANT_DUAL_AXIS || p->quantizer == SQ_QUANT_ROW_ABSMAX) &&
               p->L <= 4096 && p->H <= 4096 && shape_supported(p->dk, p->dv);
     if (ok) {
         const uint64_t nw = r.get<uint64_t>();
@@ -331,6 +339,7 @@ extern "C" sq_status sq_pool_create(const sq_plan* p, void* d_pool, size_t pool_
     pl->plan_id = p->plan_id;
     pl->L = p->L; pl->H = p->H; pl->dk = p->dk; pl->dv = p->dv; pl->form = p->form; pl->n_slots = n_slots;
     pl->n_grid = int32_t(p->grid.size());
+    pl->quantizer = p->quantizer;
     for (int g = 0; g < kMaxGrid; ++g) pl->grid[g] = g < pl->n_grid ? p->grid[g] : 1.f;
     pl->pool = static_cast<uint8_t*>(d_pool);
     pl->pool_bytes = pool_bytes;
@@ -391,6 +400,7 @@ static StepParams base_params(const sq_pool* pl, int32_t layer0, int32_t n_layer
     p.form = pl->form;
     p.slots = slots;
     p.n_grid = pl->n_grid;
+    p.quant_mode = pl->quantizer;
     p.unit_first = pl->grid[0] == 1.0f ? 1 : 0;
     for (int g = 0; g < kMaxGrid; ++g) p.grid[g] = pl->grid[g];
     return p;
@@ -403,7 +413,7 @@ extern "C" sq_status sq_state_step(sq_pool* pl, int32_t layer0, int32_t n_layers
                                    const float* d_beta, float* d_y, void* stream_main, void* stream_aux, uint32_t flags) {
     sq_status st = check_range(pl, layer0, n_layers, batch);
     if (st != SQ_OK) return st;
-    if (flags & ~(SQ_STEP_SPLIT | SQ_STEP_VALIDATE)) { set_error("unknown flags 0x%x", flags); return SQ_ERR_ARG; }
+    if (flags & ~(SQ_STEP_SPLIT | SQ_STEP_VALIDATE | SQ_STEP_NO_JOIN)) { set_error("unknown flags 0x%x", flags); return SQ_ERR_ARG; }
     if (batch == 0) return SQ_OK;
     if (!d_slots || !d_q || !d_k || !d_v || !d_gate || !d_beta || !d_y) { set_error("NULL device array"); return SQ_ERR_ARG; }
     hipStream_t sm = static_cast<hipStream_t>(stream_main);
@@ -420,22 +430,17 @@ extern "C" sq_status sq_state_step(sq_pool* pl, int32_t layer0, int32_t n_layers
         e = launch_state(pl->dk, pl->dv, kModeStep, p, n_states, sm);
         return e == hipSuccess ? SQ_OK : hip_fail(e, "state step launch");
     }
-    // split arrangement: per chunk, readout kernel on the main stream, fit + pack on the aux stream
-    const size_t need = size_t(n_states) * pl->dv;
-    if (need > pl->e_cap) {
-        if (pl->e_buf) {
-            e = hipStreamSynchronize(sm);
-            if (e == hipSuccess && sa != sm) e = hipStreamSynchronize(sa);
-            if (e != hipSuccess) return hip_fail(e, "synchronizing before growing the split scratch");
-            (void)hipFree(pl->e_buf);
-            pl->e_buf = nullptr;
-            pl->e_cap = 0;
-        }
+    // split arrangement: per chunk, readout kernel on the main stream, fit + pack on the aux stream.
+    // Scratch e = v - k^T D S: one region per (layer, request index, head), allocated once per pool.
+    const int64_t layer_stride = int64_t(pl->n_slots) * pl->H;
+    if (!pl->e_buf) {
+        const size_t need = size_t(pl->L) * size_t(layer_stride) * pl->dv;
         e = hipMalloc(reinterpret_cast<void**>(&pl->e_buf), need * sizeof(float));
         if (e != hipSuccess) { set_error("hipMalloc of the split scratch: %s", hipGetErrorString(e)); return SQ_ERR_NOMEM; }
         pl->e_cap = need;
     }
-    p.e_buf = pl->e_buf;
+    p.e_buf = pl->e_buf + size_t(layer0) * size_t(layer_stride) * pl->dv;
+    p.e_layer_stride = layer_stride;
     const int per_layer = batch * pl->H;
     const int n_chunks = n_layers > 1 ? n_layers : std::min(4, std::max(1, per_layer / 256));
     const int chunk = (n_states + n_chunks - 1) / n_chunks;
@@ -466,7 +471,7 @@ extern "C" sq_status sq_state_step(sq_pool* pl, int32_t layer0, int32_t n_layers
         e = launch_state(pl->dk, pl->dv, kModeSplitB, p, ns, sa);
         if (e != hipSuccess) return hip_fail(e, "split fit/pack launch");
     }
-    if (sa != sm) {
+    if (sa != sm && !(flags & SQ_STEP_NO_JOIN)) {
         e = hipEventRecord(pl->events[1], sa);
         if (e == hipSuccess) e = hipStreamWaitEvent(sm, pl->events[1], 0);
         if (e != hipSuccess) return hip_fail(e, "joining the aux stream");

@@ -12,6 +12,7 @@ struct sq_plan {
     int32_t form, unit, L, H, dk, dv;
     std::vector<int32_t> widths;     // ascending
     int32_t budget_milli, pivot_ppm;
+    int32_t quantizer = SQ_QUANT_DUAL_AXIS;
     std::vector<float> grid;
     // planner results, canonical order
     std::vector<double> lbar, lifetime, distortion;  // [U], [U], [U][n_widths]

@@ -74,10 +74,12 @@ struct StepParams {
     float* y;
     const float* x_in;   // pack: float states [state][d_k][d_v] (canonical rows)
     float* x_out;        // unpack: float states
-    float* e_buf;        // split arrangement: v - k^T D S per state [state][d_v]
+    float* e_buf;        // split arrangement: v - k^T D S, [layer][request index][head][d_v] from layer0
+    int64_t e_layer_stride;  // split arrangement: states per layer of e_buf (n_slots * n_heads)
     int32_t state0;      // split arrangement: first state of the chunk
     int32_t n_grid;
     int32_t unit_first;  // grid[0] == 1: the first candidate needs no clamp
+    int32_t quant_mode;  // SQ_QUANT_DUAL_AXIS or SQ_QUANT_ROW_ABSMAX
     float grid[kMaxGrid];
 };
 

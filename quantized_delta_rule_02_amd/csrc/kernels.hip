@@ -330,6 +330,13 @@ __device__ __forceinline__ void load_group(const uint8_t* gp, int lane, bool act
     }
 }
 
+// Row of the split arrangement's scratch for state sid of a call: (layer - layer0, request, head)
+// with a layer stride of n_slots * n_heads.
+__device__ __forceinline__ size_t e_index(const StepParams& a, int sid) {
+    const int per_layer = a.n_heads * a.batch;
+    return (size_t)(sid / per_layer) * (size_t)a.e_layer_stride + (size_t)(sid % per_layer);
+}
+
 // One LDS round of the column fit: KG candidates c = binary16(gamma * c0), the
 // impact-weighted error F = c^2 sum_i (sqrt(w_i) r_i)^2 (t_ij / c - Q_ij)^2 of the
 // wave's rows, combined over the waves; the best candidate so far is kept (strict <).
@@ -598,14 +605,14 @@ k_state(StepParams a) {
                 ecol[c] = e;
                 if (act && wave == 0) a.y[(size_t)sid * DV + col0 + c] = fmaf(bt * kq, e, p);
                 if constexpr (MODE == kModeSplitA) {
-                    if (act && wave == 0) a.e_buf[(size_t)sid * DV + col0 + c] = e;
+                    if (act && wave == 0) a.e_buf[e_index(a, sid) * DV + col0 + c] = e;
                 }
             }
             if constexpr (MODE == kModeSplitA) return;
         } else {
             // split arrangement, second half: e = v - k^T D S comes from the first kernel
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) ecol[c] = act ? a.e_buf[(size_t)sid * DV + col0 + c] : 0.f;
+            for (int c = 0; c < CPL; ++c) ecol[c] = act ? a.e_buf[e_index(a, sid) * DV + col0 + c] : 0.f;
         }
 
         // ---- phase 2: the updated float state X = D S + beta k e^T in registers
@@ -656,9 +663,10 @@ k_state(StepParams a) {
             const bool piv = rbits == 16;
             const float m = rm[0];
             const float w = sm.w[t];
-            float rn = 1.f;
-            if (!piv && m > 0.f) rn = scale_fp16(__builtin_sqrtf(m * __builtin_amdgcn_rcpf(w)));
             const float qmax = piv ? 0.f : (float)((1 << (rbits - 1)) - 1);
+            float rn = 1.f;
+            if (!piv && m > 0.f)   // dual-axis sqrt(m / w); the ablation's per-row absmax m / qmax
+                rn = scale_fp16(a.quant_mode == 0 ? __builtin_sqrtf(m * __builtin_amdgcn_rcpf(w)) : m / qmax);
             sm.rn[t] = rn;
             sm.fit[t] = make_float4(__builtin_amdgcn_rcpf(rn), piv ? 0.f : __builtin_sqrtf(w) * rn,
                                     piv ? 0.f : __builtin_amdgcn_rcpf(qmax), qmax);
@@ -723,7 +731,7 @@ k_state(StepParams a) {
         cbest[c] = 1.f;
         fbest[c] = __builtin_inff();
     }
-    if (hflags & kHasCodeRows) {
+    if ((hflags & kHasCodeRows) && a.quant_mode == 0) {   // per-row absmax keeps every column scale at 1
         const int n_grid = a.n_grid;
         // with gamma = 1 no code can leave its range (|X / r| <= qmax c0 and the stored c rounds c0),
         // so the first round skips the clamp of its first candidate when grid[0] == 1

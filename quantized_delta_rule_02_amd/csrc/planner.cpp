@@ -112,13 +112,24 @@ double clamp_scale(double x) { return std::min(std::max(x, 0x1p-14), 65504.0); }
 // Squared reconstruction error per key row of state X [dk][dv] quantized with
 // every row at width `bits`, impact scores w, candidate grid.  row_err += ...
 void quant_row_errors(const double* X, int dk, int dv, int bits, const double* w,
-                      const std::vector<float>& grid, double* row_err) {
+                      const std::vector<float>& grid, int quantizer, double* row_err) {
     const double qmax = std::ldexp(1.0, bits - 1) - 1.0;
     std::vector<double> r(dk), c0(dv, 0.0);
     for (int i = 0; i < dk; ++i) {
         double m = 0;
         for (int j = 0; j < dv; ++j) m = std::max(m, std::fabs(X[size_t(i) * dv + j]));
-        r[i] = (m > 0) ? fp16_round_host(clamp_scale(std::sqrt(m / w[i]))) : 1.0;
+        const double pre = quantizer == SQ_QUANT_ROW_ABSMAX ? m / qmax : std::sqrt(m / w[i]);
+        r[i] = (m > 0) ? fp16_round_host(clamp_scale(pre)) : 1.0;
+    }
+    if (quantizer == SQ_QUANT_ROW_ABSMAX) {          // per-row absmax: every column scale is 1
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) {
+                const double x = X[size_t(i) * dv + j];
+                const double Q = std::min(std::max(std::nearbyint(x / r[i]), -qmax), qmax);
+                const double err = x - r[i] * Q;
+                row_err[i] += err * err;
+            }
+        return;
     }
     for (int i = 0; i < dk; ++i)
         for (int j = 0; j < dv; ++j)
@@ -301,7 +312,7 @@ sq_status run_planner(const sq_plan_cfg& cfg, sq_plan& p) {
                 run_segment(Sst.data(), dk, dv, T, alpha.data(), tk + t0 * dk, tv + t0 * dv, tb + t0);
                 for (int wi = 0; wi < nwid; ++wi) {
                     std::fill(rowerr.begin(), rowerr.end(), 0.0);
-                    quant_row_errors(Sst.data(), dk, dv, p.widths[wi], J.w.data(), p.grid, rowerr.data());
+                    quant_row_errors(Sst.data(), dk, dv, p.widths[wi], J.w.data(), p.grid, p.quantizer, rowerr.data());
                     if (per == 1) {
                         double tot = 0;
                         for (int i = 0; i < dk; ++i) tot += rowerr[i];

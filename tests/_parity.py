@@ -103,9 +103,10 @@ class Report:
 
 def compare_step(X, y_ref, rows: quant.RowPlan, grid, y_gpu, P_gpu: quant.Packed, P_ref: quant.Packed,
                  y_tol=1e-4, scale_tie=1e-5, fit_tie=1e-5, code_tie=1e-3, max_code_ties=1e-3,
-                 xhat_tol=1e-4, pivot_tie=2e-6, x_err=None) -> Report:
+                 xhat_tol=1e-4, pivot_tie=2e-6, x_err=None, mode="dual_axis") -> Report:
     """X, y_ref: the oracle's float state and readout for the step; P_ref its packed result;
-    x_err: optional per-entry bound on the library's float32 error in X (step_error_bound)."""
+    x_err: optional per-entry bound on the library's float32 error in X (step_error_bound);
+    mode: the plan's quantizer (quant.MODES)."""
     R = Report(n_states=X.shape[0])
     piv = np.asarray(rows.pivot)
     code_row = ~piv
@@ -114,7 +115,7 @@ def compare_step(X, y_ref, rows: quant.RowPlan, grid, y_gpu, P_gpu: quant.Packed
     if not R.y_rel <= y_tol:
         R.failures.append(f"y relative L2 {R.y_rel:.3e} > {y_tol}")
     # row factors
-    r_pre, r_ref = quant.row_factors(X, rows)
+    r_pre, r_ref = quant.row_factors(X, rows) if mode == "dual_axis" else quant.row_absmax_factors(X, rows)
     r_pre_c = np.clip(r_pre, 2.0 ** -14, 65504)
     bad_r = P_gpu.r != r_ref
     tie_r = bad_r & code_row & _fp16_neighbours_tie(r_pre_c, P_gpu.r, r_ref, scale_tie)
@@ -122,28 +123,34 @@ def compare_step(X, y_ref, rows: quant.RowPlan, grid, y_gpu, P_gpu: quant.Packed
     if np.any(bad_r & ~tie_r):
         i = np.argwhere(bad_r & ~tie_r)[0]
         R.failures.append(f"row factor mismatch at {tuple(i)}: gpu {P_gpu.r[tuple(i)]} oracle {r_ref[tuple(i)]}")
-    # column scales: a candidate of the grid built on the library's row factors
-    c0 = quant.column_base(X, rows, P_gpu.r)
-    cands = quant.candidate_scales(c0, grid)
-    F = np.stack([quant.fit_objective(X, rows, P_gpu.r, cands[g], quant.codes_for(X, rows, P_gpu.r, cands[g])[0])
-                  for g in range(len(grid))])
-    Fmin = F.min(axis=0)
-    pre = np.stack([np.clip(g * c0, 2.0 ** -14, 65504) for g in grid])
-    match = np.zeros((len(grid),) + c0.shape, bool)
-    for g in range(len(grid)):
-        exact = P_gpu.c == cands[g]
-        tie = _fp16_neighbours_tie(pre[g], P_gpu.c, cands[g], scale_tie)
-        match[g] = exact | tie
-        R.c_ties += int((tie & ~exact).sum())
-    near_opt = F <= Fmin[None] * (1 + fit_tie) + 1e-300
-    ok_col = np.any(match & near_opt, axis=0) | ((c0 == 0) & (P_gpu.c == 1.0))
-    best = np.argmin(F, axis=0)
-    chose_other = ~np.take_along_axis(match, best[None], 0)[0] & ok_col & (c0 > 0)
-    R.fit_ties = int(chose_other.sum())
-    if not np.all(ok_col):
-        n, j = np.argwhere(~ok_col)[0]
-        R.failures.append(f"column scale at state {n} col {j}: gpu {P_gpu.c[n, j]} candidates "
-                          f"{cands[:, n, j]} F {F[:, n, j]}")
+    if mode == "row_absmax":
+        # no column fit: every column scale stays 1
+        if np.any(P_gpu.c != 1.0):
+            n, j = np.argwhere(P_gpu.c != 1.0)[0]
+            R.failures.append(f"column scale at state {n} col {j} is {P_gpu.c[n, j]}, not 1")
+    else:
+        # column scales: a candidate of the grid built on the library's row factors
+        c0 = quant.column_base(X, rows, P_gpu.r)
+        cands = quant.candidate_scales(c0, grid)
+        F = np.stack([quant.fit_objective(X, rows, P_gpu.r, cands[g], quant.codes_for(X, rows, P_gpu.r, cands[g])[0])
+                      for g in range(len(grid))])
+        Fmin = F.min(axis=0)
+        pre = np.stack([np.clip(g * c0, 2.0 ** -14, 65504) for g in grid])
+        match = np.zeros((len(grid),) + c0.shape, bool)
+        for g in range(len(grid)):
+            exact = P_gpu.c == cands[g]
+            tie = _fp16_neighbours_tie(pre[g], P_gpu.c, cands[g], scale_tie)
+            match[g] = exact | tie
+            R.c_ties += int((tie & ~exact).sum())
+        near_opt = F <= Fmin[None] * (1 + fit_tie) + 1e-300
+        ok_col = np.any(match & near_opt, axis=0) | ((c0 == 0) & (P_gpu.c == 1.0))
+        best = np.argmin(F, axis=0)
+        chose_other = ~np.take_along_axis(match, best[None], 0)[0] & ok_col & (c0 > 0)
+        R.fit_ties = int(chose_other.sum())
+        if not np.all(ok_col):
+            n, j = np.argwhere(~ok_col)[0]
+            R.failures.append(f"column scale at state {n} col {j}: gpu {P_gpu.c[n, j]} candidates "
+                              f"{cands[:, n, j]} F {F[:, n, j]}")
     # codes for the library's scales
     Qo, z = quant.codes_for(X, rows, P_gpu.r, P_gpu.c)
     dQ = (P_gpu.Q - Qo) * code_row[:, :, None]

@@ -35,7 +35,7 @@ def oracle_unit_bits(wl: Workload, n_layers: int, calib_segments=2, calib_len=32
 
 class Rig:
     def __init__(self, wl: Workload, n_layers: int, batch: int, unit_bits=None, n_slots=None, slots=None,
-                 oplan=None):
+                 oplan=None, mode="dual_axis"):
         import torch
         self.torch = torch
         self.wl = wl
@@ -50,7 +50,9 @@ class Rig:
         self.plan = sq.sq_plan_create(
             form=0 if wl.form == GDN else 1, unit=0 if wl.unit == UNIT_HEAD else 1, n_layers=n_layers,
             n_heads=wl.n_heads, d_k=wl.d_k, d_v=wl.d_v, widths=wl.widths, budget_milli=wl.budget_milli,
-            pivot_ppm=wl.pivot_ppm, grid=wl.grid, gate=self.gates, impact=self.impact, unit_bits=self.unit_bits)
+            pivot_ppm=wl.pivot_ppm, grid=wl.grid, gate=self.gates, impact=self.impact, unit_bits=self.unit_bits,
+            quantizer=quant.MODES.index(mode))
+        self.mode = mode
         row_bits, w = sq.sq_plan_rows(self.plan)
         self.row_bits = row_bits
         self.n_slots = n_slots if n_slots is not None else batch

@@ -144,6 +144,38 @@ def test_step_teacher_forced(torch, name, wl, nL, B, T):
     rig.close()
 
 
+ABSMAX = [("gdn", configs.GDN_DECODE, 1, 2, 3), ("kda", configs.KDA_DECODE, 1, 2, 3),
+          ("outlier", configs.OUTLIER, 1, 1, 2)]
+
+
+@pytest.mark.parametrize("name,wl,nL,B,T", ABSMAX, ids=[c[0] for c in ABSMAX])
+def test_row_absmax_quantizer_pack_and_steps(torch, name, wl, nL, B, T):
+    """The ablation's per-row absmax quantizer: pack and teacher-forced steps against the oracle."""
+    import quantized_delta_rule_02_amd as sq
+    say(f"row absmax {name}: layers={nL} batch={B} steps={T}")
+    rig = _rig(wl, nL, B, mode="row_absmax")
+    X = rig.warm_state(steps=min(wl.warmup_steps, 64)).astype(np.float32).astype(np.float64)
+    sq.sq_pack(rig.pool, 0, nL, B, rig.slots, rig._t(X.reshape(-1), torch.float32))
+    torch.cuda.synchronize()
+    P = quant.quantize(X, rig.rows, wl.grid, mode="row_absmax")
+    zeros = np.zeros((rig.N, rig.dv))
+    R = compare_step(X, zeros, rig.rows, wl.grid, zeros, rig.export_packed(), P, mode="row_absmax")
+    assert R.ok(), f"pack: {R.failures}"
+    q, k, v, beta = rig.inputs(T)
+    alpha = rig.alpha_states()
+    for t in range(T):
+        rig.import_packed(P)
+        y_g = rig.step(q[t], k[t], v[t], beta[t])
+        Pg = rig.export_packed()
+        P2, y, Xo = packed_step(P, rig.rows, q[t], k[t], v[t], alpha, beta[t], wl.grid, mode="row_absmax")
+        R = compare_step(Xo, y, rig.rows, wl.grid, y_g, Pg, P2, mode="row_absmax",
+                         x_err=step_error_bound(P, rig.rows, k[t], v[t], alpha, beta[t]))
+        assert R.ok(), f"step {t}: {R.failures}"
+        P = P2
+    say(name, R)
+    rig.close()
+
+
 def test_split_arrangement_is_bitwise_fused(torch):
     """Readout kernel on one stream, fit + pack on another: identical bytes and readout."""
     wl = configs.GDN_DECODE
@@ -161,6 +193,46 @@ def test_split_arrangement_is_bitwise_fused(torch):
     for ys, mem in outs[1:]:
         assert all(np.array_equal(a, b) for a, b in zip(ys, outs[0][0]))
         assert torch.equal(mem, outs[0][1])
+    rig.close()
+
+
+def test_split_without_join_per_layer_equals_fused(torch):
+    """Per-layer split calls that leave the fit running on the second stream (the caller joins once
+    per step) give the same bytes and readout as one fused call over all layers."""
+    import quantized_delta_rule_02_amd as sq
+    wl = configs.SERVING_6
+    nL, B = 3, 2
+    say("split no-join per layer vs fused serving6")
+    rig = _rig(wl, nL, B)
+    P = quant.quantize(rig.warm_state(steps=32), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(2)
+    per = B * rig.H
+    t = lambda a: rig._t(np.ascontiguousarray(a).reshape(-1), torch.float32)
+    gate = rig.gate_step()       # [layers][requests][heads] (GDN)
+    results = []
+    for per_layer in (False, True):
+        rig.import_packed(P)
+        aux = torch.cuda.Stream()
+        ys = []
+        for s in range(2):
+            # inputs stay alive until the synchronization: the second stream reads them too
+            qs, ks, vs, bs = t(q[s]), t(k[s]), t(v[s]), t(beta[s])
+            y = torch.zeros(rig.N * rig.dv, dtype=torch.float32, device="cuda")
+            if not per_layer:
+                sq.sq_state_step(rig.pool, 0, nL, B, rig.slots, qs, ks, vs, gate, bs, y)
+            else:
+                dk, dv = rig.dk, rig.dv
+                for l in range(nL):
+                    a0, a1 = l * per, (l + 1) * per
+                    sq.sq_state_step(rig.pool, l, 1, B, rig.slots, qs[a0 * dk:a1 * dk], ks[a0 * dk:a1 * dk],
+                                     vs[a0 * dv:a1 * dv], gate[a0:a1], bs[a0:a1], y[a0 * dv:a1 * dv],
+                                     stream_aux=aux, flags=sq.SQ_STEP_SPLIT | sq.SQ_STEP_NO_JOIN)
+                torch.cuda.current_stream().wait_stream(aux)
+            torch.cuda.synchronize()
+            ys.append(y.cpu().numpy())
+        results.append((ys, rig.mem.clone()))
+    assert all(np.array_equal(a, b) for a, b in zip(results[0][0], results[1][0]))
+    assert torch.equal(results[0][1], results[1][1])
     rig.close()
 
 

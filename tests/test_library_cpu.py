@@ -12,6 +12,7 @@ import pytest
 import quantized_delta_rule_02_amd as sq
 from quantized_delta_rule_02_amd import _lib
 from oracle import planner as oplanner
+from oracle import quant as oquant
 from workloads import configs, gen
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,23 +53,26 @@ def test_calibration_generator_matches_numpy_generator():
             assert np.mean(x == y) > 0.99
 
 
-CASES = [("tiny", configs.TINY, 1, 2, 16), ("gdn", configs.GDN_DECODE, 1, 2, 24),
-         ("kda", configs.KDA_DECODE, 1, 2, 16), ("serving", configs.SERVING_6, 2, 1, 16),
-         ("outlier", configs.OUTLIER, 1, 1, 12)]
+CASES = [("tiny", configs.TINY, 1, 2, 16, 0), ("gdn", configs.GDN_DECODE, 1, 2, 24, 0),
+         ("kda", configs.KDA_DECODE, 1, 2, 16, 0), ("serving", configs.SERVING_6, 2, 1, 16, 0),
+         ("outlier", configs.OUTLIER, 1, 1, 12, 0), ("gdn-row-absmax", configs.GDN_DECODE, 1, 2, 24, 1),
+         ("kda-row-absmax", configs.KDA_DECODE, 1, 2, 16, 1)]
 
 
-@pytest.mark.parametrize("name,wl,nL,S,T", CASES, ids=[c[0] for c in CASES])
-def test_cpp_planner_matches_oracle_planner(name, wl, nL, S, T):
+@pytest.mark.parametrize("name,wl,nL,S,T,qz", CASES, ids=[c[0] for c in CASES])
+def test_cpp_planner_matches_oracle_planner(name, wl, nL, S, T, qz):
     seed = gen.calib_seed(wl)
     tr = {(l, h): gen.calib_traces(seed, l, h, S, T, wl.d_k, wl.d_v) for l in range(nL) for h in range(wl.n_heads)}
     stack = lambda i: np.stack([np.stack([tr[(l, h)][i] for h in range(wl.n_heads)]) for l in range(nL)])
     calib = tuple(stack(i) for i in range(4))
     imp = gen.impact_scores(wl)[:nL]
     p = sq.sq_plan_create(**_plan_kw(wl, nL), impact=imp, calib=calib, calib_segments=S, calib_len=T,
-                          n_threads=4)
+                          n_threads=4, quantizer=qz)
+    assert p.desc["quantizer"] == qz
     u = sq.sq_plan_units(p)
     o = oplanner.make_plan(wl.form, wl.unit, nL, wl.n_heads, wl.d_k, wl.d_v, wl.widths, wl.budget_milli,
-                           wl.pivot_ppm, wl.grid, gen.unit_gates(wl)[:nL], lambda l, h: tr[(l, h)], impact=imp)
+                           wl.pivot_ppm, wl.grid, gen.unit_gates(wl)[:nL], lambda l, h: tr[(l, h)], impact=imp,
+                           mode=oquant.MODES[qz])
     assert np.allclose(u["lbar"], o.lbar, rtol=1e-12, atol=0)
     assert np.allclose(u["lifetime"], o.L, rtol=1e-12, atol=0)
     assert np.allclose(u["distortion"], o.D, rtol=1e-9, atol=1e-300)
@@ -138,7 +142,8 @@ def test_argument_validation_status_codes():
     kw = _plan_kw(wl, 1)
     kw.update(impact=gen.impact_scores(wl)[:1], unit_bits=np.full(32, 6, np.int32))
     for bad, status in ((dict(form=2), -1), (dict(unit=5), -1), (dict(d_k=96, impact=None), -3), (dict(widths=(4, 5)), -3),
-                        (dict(widths=(4, 4)), -1), (dict(grid=[]), None), (dict(pivot_ppm=-1), -1)):
+                        (dict(widths=(4, 4)), -1), (dict(grid=[]), None), (dict(pivot_ppm=-1), -1),
+                        (dict(quantizer=2), -1)):
         args = dict(kw)
         args.update(bad)
         if status is None:
@@ -174,10 +179,11 @@ def test_argument_validation_status_codes():
     assert sq.StepQError(-1, "x").status == -1
 
 
-def test_plan_save_load_roundtrip():
+@pytest.mark.parametrize("qz", [0, 1])
+def test_plan_save_load_roundtrip(qz):
     wl = configs.KDA_DECODE
     p = sq.sq_plan_create(**_plan_kw(wl, 1), impact=gen.impact_scores(wl)[:1], calib_seed=3, calib_segments=1,
-                          calib_len=8)
+                          calib_len=8, quantizer=qz)
     blob = sq.sq_plan_save(p)
     q = sq.sq_plan_load(blob)
     assert q.desc == p.desc

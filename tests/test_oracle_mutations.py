@@ -73,6 +73,20 @@ def _impact_without_gate(q, k, beta, alpha_head):
     return np.mean(a * a, axis=0)
 
 
+def _row_absmax_power_of_two(X, rows, scale_fp16=True):
+    m = np.max(np.abs(X), axis=2)
+    r_pre = m / (2.0 ** (np.asarray(rows.bits, np.float64) - 1.0))
+    r = quant._scale_round(r_pre, scale_fp16)
+    return r_pre, np.where(rows.pivot, 1.0, np.where(m > 0, r, 1.0))
+
+
+def _row_absmax_half_range(X, rows, scale_fp16=True):
+    m = np.max(np.abs(X), axis=2)
+    r_pre = 2.0 * m / rows.qmax
+    r = quant._scale_round(r_pre, scale_fp16)
+    return r_pre, np.where(rows.pivot, 1.0, np.where(m > 0, r, 1.0))
+
+
 def _allocate_widest_first(cost, widths, budget_milli):
     return np.full(cost.shape[0], len(widths) - 1)
 
@@ -92,6 +106,10 @@ CASES = [
      lambda: tq.test_column_fit_equals_brute_force(4, 4, 4)),
     ("column base without qmax", [(quant, "column_base", _column_base_without_qmax)],
      tq.test_rank_one_closed_form),
+    ("row absmax over 2^(b-1)", [(quant, "row_absmax_factors", _row_absmax_power_of_two)],
+     tq.test_row_absmax_half_step_bound_zero_rows_and_pivots),
+    ("row absmax at half range", [(quant, "row_absmax_factors", _row_absmax_half_range)],
+     tq.test_row_absmax_half_step_bound_zero_rows_and_pivots),
     ("linear lifetime", [(planner, "lifetime_weight", _lifetime_linear)],
      tp.test_lifetime_closed_form_for_constant_gate),
     ("impact without gate", [(planner, "impact_from_traces", _impact_without_gate)],

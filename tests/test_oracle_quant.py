@@ -220,3 +220,50 @@ def test_int8_comparator_matches_library_per_channel_quantization():
         assert np.max(np.abs(ref - Q[n])) <= 1          # the library divides in float32
         diffs += int(np.sum(ref != Q[n]))
     assert diffs <= 2
+
+
+# ---------------------------------------------------------------- per-row absmax quantizer (ablation)
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_row_absmax_matches_library_fake_quantization(bits):
+    """Per-row absmax codes = the library's per-channel symmetric quantization with the same
+    (binary16-rounded) scales; the library divides in float32, so codes may differ by one
+    level where the quotient sits at a half-integer."""
+    torch = pytest.importorskip("torch")
+    X = _state(21 + bits, N=4, dk=16, dv=48, scale=2.0).astype(np.float32).astype(np.float64)
+    rows = _rows(4, 16, bits)
+    P = quant.quantize(X, rows, GRID4, mode="row_absmax")
+    qm = 2 ** (bits - 1) - 1
+    assert np.all(P.c == 1.0)
+    diffs = 0
+    for n in range(4):
+        t = torch.tensor(X[n], dtype=torch.float32)
+        ref = torch.fake_quantize_per_channel_affine(t, torch.tensor(P.r[n], dtype=torch.float32),
+                                                     torch.zeros(16, dtype=torch.int32), 0, -qm, qm)
+        Qref = np.rint(ref.numpy().astype(np.float64) / P.r[n][:, None])
+        assert np.max(np.abs(Qref - P.Q[n])) <= 1
+        diffs += int(np.sum(Qref != P.Q[n]))
+    assert diffs <= 2
+
+
+def test_row_absmax_half_step_bound_zero_rows_and_pivots():
+    X = _state(31, N=3, dk=8, dv=16, scale=4.0)
+    X[0, 2] = 0.0
+    rows = _rows(3, 8, 6)
+    rows.pivot[:, 5] = True
+    rows.bits[:, 5] = 16
+    P = quant.quantize(X, rows, GRID4, mode="row_absmax")
+    Xh = quant.dequantize(P, rows)
+    code = ~rows.pivot
+    err = np.abs(X - Xh)
+    # the scale covers the row without clipping (half-step bound everywhere) and uses the full
+    # range: the row's largest entry takes the extreme code
+    assert np.all((err <= P.r[:, :, None] / 2 + 1e-12)[code])
+    imax = np.argmax(np.abs(X), axis=2)
+    top = np.abs(np.take_along_axis(P.Q, imax[:, :, None], axis=2)[:, :, 0])
+    live = code & (np.max(np.abs(X), axis=2) > 0)
+    assert np.all(top[live] == rows.qmax[live])
+    assert P.r[0, 2] == 1.0 and np.all(P.Q[0, 2] == 0)
+    assert np.all(P.r[:, 5] == 1.0) and np.array_equal(P.V[:, 5], fp16_round(X[:, 5]))
+    with pytest.raises(ValueError):
+        quant.quantize(X, rows, GRID4, mode="row_max")

@@ -98,3 +98,16 @@ def test_compare_accepts_oracle_and_rejects_planted_mistakes():
 
     for what in ["code", "pivot", "r", "c", "y"]:
         assert not planted(**{what: True}).ok(), what
+
+
+def test_compare_in_row_absmax_mode():
+    grid = (1.0, 0.875, 0.75, 0.625)
+    rows, P, q, k, v, a, b = _case(4)
+    P2, y, X = packed_step(P, rows, q, k, v, a, b, grid, mode="row_absmax")
+    assert np.all(P2.c == 1.0)
+    assert compare_step(X, y, rows, grid, y.copy(), P2, P2, mode="row_absmax").ok()
+    bad = quant.Packed(Q=P2.Q, r=P2.r, c=P2.c.copy(), V=P2.V)
+    bad.c[0, 3] = 0.875
+    assert not compare_step(X, y, rows, grid, y.copy(), bad, P2, mode="row_absmax").ok()
+    # the dual-axis comparison rejects a row-absmax result (different row factors)
+    assert not compare_step(X, y, rows, grid, y.copy(), P2, P2).ok()
