@@ -59,7 +59,7 @@ typedef int32_t sq_status;
 #define SQ_QUANT_DUAL_AXIS 0      /* row factors sqrt(m / w) + impact-weighted column fit (the method) */
 #define SQ_QUANT_ROW_ABSMAX 1     /* per-row absmax r = m / qmax, column scales 1 (ablation: no fit) */
 
-#define SQ_MAX_WIDTHS 4
+#define SQ_MAX_WIDTHS 8
 #define SQ_MAX_GRID   8
 #define SQ_PIVOT_BITS 16          /* width reported for a pivot (binary16) unit/row  */
 
@@ -68,7 +68,7 @@ typedef struct sq_plan_cfg {
     int32_t form;                 /* SQ_FORM_GDN or SQ_FORM_KDA */
     int32_t unit;                 /* SQ_UNIT_HEAD or SQ_UNIT_ROW */
     int32_t n_layers, n_heads, d_k, d_v;
-    int32_t n_widths;             /* candidate code widths, each in {4, 6, 8} */
+    int32_t n_widths;             /* candidate code widths, each in {2, 3, 4, 6, 8} */
     int32_t widths[SQ_MAX_WIDTHS];
     int32_t budget_milli;         /* average bits x 1000 over non-pivot units */
     int32_t pivot_ppm;            /* pivot units: ceil(pivot_ppm * units / 1e6) */
@@ -76,7 +76,7 @@ typedef struct sq_plan_cfg {
     float   grid[SQ_MAX_GRID];
     const float* gate;            /* alpha per unit for calibration: [L][H] (GDN) or [L][H][d_k] (KDA) */
     const float* impact;          /* row-impact score w [L][H][d_k]; NULL = estimate from the traces */
-    const int32_t* unit_bits;     /* optional fixed allocation per unit (4/6/8, 16 = pivot); NULL = plan */
+    const int32_t* unit_bits;     /* optional fixed allocation per unit (a candidate width, 16 = pivot); NULL = plan */
     /* calibration traces; NULL q = draw them with the built-in Philox-4x32-10 generator */
     const float* calib_q;         /* [L][H][S][T][d_k] */
     const float* calib_k;         /* [L][H][S][T][d_k] */

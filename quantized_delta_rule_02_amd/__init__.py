@@ -77,7 +77,7 @@ def sq_plan_create(*, form, unit, n_layers, n_heads, d_k, d_v, widths, budget_mi
     cfg.n_layers, cfg.n_heads, cfg.d_k, cfg.d_v = int(n_layers), int(n_heads), int(d_k), int(d_v)
     widths = list(widths)
     if not 1 <= len(widths) <= _lib.SQ_MAX_WIDTHS:
-        raise ValueError("between 1 and 4 candidate widths")
+        raise ValueError(f"between 1 and {_lib.SQ_MAX_WIDTHS} candidate widths")
     cfg.n_widths = len(widths)
     for i, b in enumerate(widths):
         cfg.widths[i] = int(b)

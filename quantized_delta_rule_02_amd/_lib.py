@@ -16,7 +16,7 @@ SQ_UNIT_HEAD, SQ_UNIT_ROW = 0, 1
 SQ_QUANT_DUAL_AXIS, SQ_QUANT_ROW_ABSMAX = 0, 1
 SQ_STEP_SPLIT, SQ_STEP_VALIDATE, SQ_STEP_NO_JOIN = 1, 2, 4
 SQ_PIVOT_BITS = 16
-SQ_MAX_WIDTHS, SQ_MAX_GRID = 4, 8
+SQ_MAX_WIDTHS, SQ_MAX_GRID = 8, 8
 
 
 class SqPlanCfg(ctypes.Structure):

@@ -43,6 +43,7 @@ using namespace sq;
 struct sq_pool {
     uint64_t plan_id;
     int32_t L, H, dk, dv, form, n_slots, n_grid, quantizer;
+    int32_t narrow;                  // some group uses a 2- or 3-bit container
     float grid[kMaxGrid];
     uint8_t* pool;
     size_t pool_bytes;
@@ -94,7 +95,10 @@ static sq_status validate_cfg(const sq_plan_cfg* c) {
     if (c->n_widths < 1 || c->n_widths > SQ_MAX_WIDTHS) { set_error("n_widths %d", c->n_widths); return SQ_ERR_ARG; }
     for (int i = 0; i < c->n_widths; ++i) {
         const int b = c->widths[i];
-        if (b != 4 && b != 6 && b != 8) { set_error("width %d not in {4, 6, 8}", b); return SQ_ERR_UNSUPPORTED; }
+        if (b != 2 && b != 3 && b != 4 && b != 6 && b != 8) {
+            set_error("width %d not in {2, 3, 4, 6, 8}", b);
+            return SQ_ERR_UNSUPPORTED;
+        }
         for (int j = 0; j < i; ++j)
             if (c->widths[j] == b) { set_error("width %d repeated", b); return SQ_ERR_ARG; }
     }
@@ -269,7 +273,7 @@ extern "C" sq_status sq_plan_load(const void* buf, size_t bytes, sq_plan** out) 
         }
         if (ok)
             for (int32_t b : p->row_bits)
-                if (b != 4 && b != 6 && b != 8 && b != SQ_PIVOT_BITS) ok = false;
+                if (b != 2 && b != 3 && b != 4 && b != 6 && b != 8 && b != SQ_PIVOT_BITS) ok = false;
         if (ok)
             for (float w : p->impact)
                 if (!(w > 0.f) || !std::isfinite(w)) ok = false;
@@ -340,6 +344,7 @@ extern "C" sq_status sq_pool_create(const sq_plan* p, void* d_pool, size_t pool_
     pl->L = p->L; pl->H = p->H; pl->dk = p->dk; pl->dv = p->dv; pl->form = p->form; pl->n_slots = n_slots;
     pl->n_grid = int32_t(p->grid.size());
     pl->quantizer = p->quantizer;
+    pl->narrow = std::any_of(p->grp_bits.begin(), p->grp_bits.end(), [](uint8_t b) { return b <= 3; }) ? 1 : 0;
     for (int g = 0; g < kMaxGrid; ++g) pl->grid[g] = g < pl->n_grid ? p->grid[g] : 1.f;
     pl->pool = static_cast<uint8_t*>(d_pool);
     pl->pool_bytes = pool_bytes;
@@ -401,6 +406,7 @@ static StepParams base_params(const sq_pool* pl, int32_t layer0, int32_t n_layer
     p.slots = slots;
     p.n_grid = pl->n_grid;
     p.quant_mode = pl->quantizer;
+    p.narrow = pl->narrow;
     p.unit_first = pl->grid[0] == 1.0f ? 1 : 0;
     for (int g = 0; g < kMaxGrid; ++g) p.grid[g] = pl->grid[g];
     return p;

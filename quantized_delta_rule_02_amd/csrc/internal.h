@@ -6,10 +6,14 @@
 //   storage rows [w*RPW, (w+1)*RPW); lane l (< LPR) owns the CPL adjacent value
 //   columns [l*CPL, (l+1)*CPL).  A "group" is GR = 16/CPL consecutive storage
 //   rows, i.e. 16 entries per lane.  Inside a record the groups come first, in
-//   storage-row order; group g of width b (4, 6, 8 or 16 bits) occupies
-//   LPR * 2b bytes, lane l's 16 entries at byte l*2b (b/2 dwords), so one wave
-//   reads or writes a group with one contiguous vector access.  Entry e = r*CPL + c
+//   storage-row order; group g of width b (2, 3, 4, 6, 8 or 16 bits) occupies
+//   LPR * 2b bytes, lane l's 16 entries at byte l*2b (b/2 dwords; for b = 3 a
+//   dword at l*4 and a 16-bit plane at LPR*4 + l*2), so one wave reads or
+//   writes a group with contiguous vector accesses.  Entry e = r*CPL + c
 //   (r = row inside the group, c = column inside the lane) is placed as:
+//     2-bit : bits 8(e%4) + 2(e/4) of the dword         (Q + 2)
+//     3-bit : low two bits as for 2-bit; the third bit at bit 4(e%4) + e/4 of
+//             the 16-bit plane                          (Q + 4)
 //     8-bit : byte e                                   (biased code Q + 128)
 //     4-bit : dword e/8, byte e%4, high nibble if (e%8) >= 4  (Q + 8)
 //     6-bit : e < 12: low 6 bits of byte (e%4) of dword e/4;
@@ -20,8 +24,8 @@
 //   After the groups: binary16 row factors [d_k] (storage order), binary16
 //   column scales [d_v]; the record is padded to 256 bytes.
 //
-//   Storage row order: pivot rows first, then 8-, 6- and 4-bit rows, each in
-//   canonical order.  A group's storage width is the widest of its rows (a row
+//   Storage row order: pivot rows first, then rows by descending width, each
+//   width in canonical order.  A group's storage width is the widest of its rows (a row
 //   keeps its own code range; only the container is wider), so at most a few
 //   groups per head use a wider container than their rows need.
 #pragma once
@@ -50,7 +54,7 @@ constexpr uint8_t kHasPivotRows = 2;
 struct DevTables {
     const uint64_t* rec_off;    // [LH] byte offset of the record inside a slot
     const uint32_t* grp_off;    // [LH][NG] byte offset of each group inside the record
-    const uint8_t* grp_bits;    // [LH][NG] container width 4/6/8/16
+    const uint8_t* grp_bits;    // [LH][NG] container width 2/3/4/6/8/16
     const uint32_t* scale_off;  // [LH] byte offset of the binary16 row factors (column scales follow)
     const uint16_t* perm;       // [LH][d_k] storage row -> canonical row
     const uint8_t* row_bits;    // [LH][d_k] code width of the row, 16 = pivot (storage order)
@@ -80,6 +84,7 @@ struct StepParams {
     int32_t n_grid;
     int32_t unit_first;  // grid[0] == 1: the first candidate needs no clamp
     int32_t quant_mode;  // SQ_QUANT_DUAL_AXIS or SQ_QUANT_ROW_ABSMAX
+    int32_t narrow;      // the plan has 2- or 3-bit containers
     float grid[kMaxGrid];
 };
 

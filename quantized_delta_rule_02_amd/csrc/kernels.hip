@@ -89,6 +89,36 @@ __device__ __forceinline__ void unpack8(const uint32_t* d, float* o) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] = (float)((d[e >> 2] >> (8 * (e & 3))) & 0xFFu);
 }
+// 2-bit: entry e = 4k + j at bits 8j + 2k of one dword.  3-bit: the low two bits likewise, the
+// third bit of entry 4k + j at bit 4j + k of a 16-bit plane (internal.h).
+__device__ __forceinline__ void unpack2(uint32_t lo, float* o) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = (float)((lo >> (8 * (e & 3) + 2 * (e >> 2))) & 3u);
+}
+__device__ __forceinline__ void unpack3(uint32_t lo, uint32_t hi, float* o) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int j = e & 3, k = e >> 2;
+        o[e] = (float)(((lo >> (8 * j + 2 * k)) & 3u) | (((hi >> (4 * j + k)) & 1u) << 2));
+    }
+}
+__device__ __forceinline__ void pack2(const int* c, uint32_t* lo) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x |= (uint32_t)(c[e] & 3) << (8 * (e & 3) + 2 * (e >> 2));
+    *lo = x;
+}
+__device__ __forceinline__ void pack3(const int* c, uint32_t* lo, uint32_t* hi) {
+    uint32_t x = 0, h = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int j = e & 3, k = e >> 2;
+        x |= (uint32_t)(c[e] & 3) << (8 * j + 2 * k);
+        h |= (uint32_t)((c[e] >> 2) & 1) << (4 * j + k);
+    }
+    *lo = x;
+    *hi = h;
+}
 __device__ __forceinline__ void pack4(const int* c, uint32_t* d) {
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
@@ -293,6 +323,25 @@ __device__ __forceinline__ void unpack6f(const uint32_t* d, float* o) {
     for (int k = 0; k < 4; ++k) o[12 + k] = (float)((p >> (8 * k)) & 0xFFu);
 }
 
+__device__ __forceinline__ void unpack2f(uint32_t lo, float* o) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t x = (lo >> (2 * k)) & 0x03030303u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[4 * k + j] = (float)((x >> (8 * j)) & 0xFFu);
+    }
+}
+__device__ __forceinline__ void unpack3f(uint32_t lo, uint32_t hi, float* o) {
+    // nibble j of the plane -> low nibble of byte j
+    const uint32_t H = (hi & 0xFu) | ((hi << 4) & 0xF00u) | ((hi << 8) & 0xF0000u) | ((hi << 12) & 0xF000000u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t x = ((lo >> (2 * k)) & 0x03030303u) | (((H >> k) & 0x01010101u) << 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[4 * k + j] = (float)((x >> (8 * j)) & 0xFFu);
+    }
+}
+
 // pack 16 magic-rounded codes (the code sits in the low bits of each float's pattern)
 __device__ __forceinline__ void pack4m(const float* m, uint32_t* d) {
 #pragma unroll
@@ -313,6 +362,26 @@ __device__ __forceinline__ void pack6m(const float* m, uint32_t* d) {
                                    __float_as_uint(m[4 * w + 2]), __float_as_uint(m[4 * w + 3]));
         d[w] = ((p << (6 - 2 * w)) & 0xC0C0C0C0u) | b;
     }
+}
+__device__ __forceinline__ void pack2m(const float* m, uint32_t* lo) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        x |= (gather4(__float_as_uint(m[4 * k]), __float_as_uint(m[4 * k + 1]), __float_as_uint(m[4 * k + 2]),
+                      __float_as_uint(m[4 * k + 3])) & 0x03030303u) << (2 * k);
+    *lo = x;
+}
+__device__ __forceinline__ void pack3m(const float* m, uint32_t* lo, uint32_t* hi) {
+    uint32_t x = 0, H = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t g = gather4(__float_as_uint(m[4 * k]), __float_as_uint(m[4 * k + 1]),
+                                   __float_as_uint(m[4 * k + 2]), __float_as_uint(m[4 * k + 3]));
+        x |= (g & 0x03030303u) << (2 * k);
+        H |= ((g >> 2) & 0x01010101u) << k;
+    }
+    *lo = x;
+    *hi = (H & 0xFu) | ((H >> 4) & 0xF0u) | ((H >> 8) & 0xF00u) | ((H >> 12) & 0xF000u);
 }
 __device__ __forceinline__ void pack8m(const float* m, uint32_t* d) {
 #pragma unroll
@@ -404,7 +473,9 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
     }
 }
 
-template <int DK, int DV, int MODE, int KG>
+// NARROW: the plan has 2- or 3-bit containers (their unpack and pack paths are compiled in only
+// then; the extra uniform branches cost the 4/6/8-bit step about 5%).
+template <int DK, int DV, int MODE, int KG, bool NARROW>
 __global__ void __launch_bounds__(nw_of(DK, DV) * 64, STEP_WAVES_PER_EU)
 k_state(StepParams a) {
     using Sh = Shape<DK, DV>;
@@ -442,7 +513,9 @@ k_state(StepParams a) {
         gb[g] = uniform(gbits[wave * GPW + g]);
         if constexpr (MODE != kModePack) {
             const uint8_t* gp = rec + uniform(goff[wave * GPW + g]);
-            if (act) load_dw<4>(gp + lane * 2 * gb[g], raw[g]);
+            // one unconditional load per group (a branch here would make the compiler wait for it);
+            // a 3-bit lane's dword sits at stride 4, its third-bit plane is loaded in phase 1
+            if (act) load_dw<4>(gp + lane * ((NARROW && gb[g] == 3) ? 4 : 2 * gb[g]), raw[g]);
             else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) raw[g][i] = 0;
@@ -513,6 +586,12 @@ k_state(StepParams a) {
         for (int g = 0; g < GPW; ++g) {
             float* xg = &X[16 * g];
             if (gb[g] == 4) unpack4f(raw[g], xg);
+            else if (NARROW && gb[g] == 2) unpack2f(raw[g][0], xg);
+            else if (NARROW && gb[g] == 3) {
+                const uint32_t hi = act ? *reinterpret_cast<const uint16_t*>(rec + uniform(goff[wave * GPW + g]) +
+                                                                           LPR * 4 + lane * 2) : 0u;
+                unpack3f(raw[g][0], hi, xg);
+            }
             else if (gb[g] == 6) unpack6f(raw[g], xg);
             else if (gb[g] == 8) unpack8(raw[g], xg);
             else {
@@ -768,6 +847,14 @@ k_state(StepParams a) {
             }
         }
         if (sb == 4) { pack4m(m, d); if (act) store_dw<2>(gp + lane * 8, d); }
+        else if (NARROW && sb == 2) { pack2m(m, d); if (act) *reinterpret_cast<uint32_t*>(gp + lane * 4) = d[0]; }
+        else if (NARROW && sb == 3) {
+            pack3m(m, d, d + 1);
+            if (act) {
+                *reinterpret_cast<uint32_t*>(gp + lane * 4) = d[0];
+                *reinterpret_cast<uint16_t*>(gp + LPR * 4 + lane * 2) = (uint16_t)d[1];
+            }
+        }
         else if (sb == 6) { pack6m(m, d); if (act) store_dw<3>(gp + lane * 12, d); }
         else if (sb == 8) { pack8m(m, d); if (act) store_dw<4>(gp + lane * 16, d); }
         else {
@@ -825,6 +912,10 @@ k_codec(CodecParams a) {
                 } else {
                     float f[16];
                     if (sb == 4) { load_dw<2>(gp + lane * 8, d); unpack4(d, f); }
+                    else if (sb == 2) unpack2(*reinterpret_cast<const uint32_t*>(gp + lane * 4), f);
+                    else if (sb == 3)
+                        unpack3(*reinterpret_cast<const uint32_t*>(gp + lane * 4),
+                                *reinterpret_cast<const uint16_t*>(gp + LPR * 4 + lane * 2), f);
                     else if (sb == 6) { load_dw<3>(gp + lane * 12, d); unpack6(d, f); }
                     else { load_dw<4>(gp + lane * 16, d); unpack8(d, f); }
 #pragma unroll
@@ -852,6 +943,12 @@ k_codec(CodecParams a) {
                     }
                 }
                 if (sb == 4) { pack4(code, d); store_dw<2>(gp + lane * 8, d); }
+                else if (sb == 2) { pack2(code, d); *reinterpret_cast<uint32_t*>(gp + lane * 4) = d[0]; }
+                else if (sb == 3) {
+                    pack3(code, d, d + 1);
+                    *reinterpret_cast<uint32_t*>(gp + lane * 4) = d[0];
+                    *reinterpret_cast<uint16_t*>(gp + LPR * 4 + lane * 2) = (uint16_t)d[1];
+                }
                 else if (sb == 6) { pack6(code, d); store_dw<3>(gp + lane * 12, d); }
                 else if (sb == 8) { pack8(code, d); store_dw<4>(gp + lane * 16, d); }
                 else {
@@ -1050,18 +1147,24 @@ __global__ void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, s
 
 // ---------------------------------------------------------------- launchers
 
-template <int DK, int DV, int KG>
-static hipError_t launch_state_kg(int mode, const StepParams& p, int n_states, hipStream_t s) {
+template <int DK, int DV, int KG, bool NARROW>
+static hipError_t launch_state_kgn(int mode, const StepParams& p, int n_states, hipStream_t s) {
     const dim3 blk(Shape<DK, DV>::NW * 64);
     switch (mode) {
-        case kModeStep: k_state<DK, DV, kModeStep, KG><<<n_states, blk, 0, s>>>(p); break;
-        case kModePack: k_state<DK, DV, kModePack, KG><<<n_states, blk, 0, s>>>(p); break;
-        case kModeUnpack: k_state<DK, DV, kModeUnpack, 1><<<n_states, blk, 0, s>>>(p); break;
-        case kModeSplitA: k_state<DK, DV, kModeSplitA, 1><<<n_states, blk, 0, s>>>(p); break;
-        case kModeSplitB: k_state<DK, DV, kModeSplitB, KG><<<n_states, blk, 0, s>>>(p); break;
+        case kModeStep: k_state<DK, DV, kModeStep, KG, NARROW><<<n_states, blk, 0, s>>>(p); break;
+        case kModePack: k_state<DK, DV, kModePack, KG, NARROW><<<n_states, blk, 0, s>>>(p); break;
+        case kModeUnpack: k_state<DK, DV, kModeUnpack, 1, NARROW><<<n_states, blk, 0, s>>>(p); break;
+        case kModeSplitA: k_state<DK, DV, kModeSplitA, 1, NARROW><<<n_states, blk, 0, s>>>(p); break;
+        case kModeSplitB: k_state<DK, DV, kModeSplitB, KG, NARROW><<<n_states, blk, 0, s>>>(p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int DK, int DV, int KG>
+static hipError_t launch_state_kg(int mode, const StepParams& p, int n_states, hipStream_t s) {
+    return p.narrow ? launch_state_kgn<DK, DV, KG, true>(mode, p, n_states, s)
+                    : launch_state_kgn<DK, DV, KG, false>(mode, p, n_states, s);
 }
 
 // candidates per LDS round: one or two when the grid is that small, otherwise four

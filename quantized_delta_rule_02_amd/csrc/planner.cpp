@@ -428,7 +428,7 @@ sq_status build_layout(sq_plan& p) {
     p.scale_off.assign(LH, 0);
     p.rec_off.assign(LH, 0);
     p.head_flags.assign(LH, 0);
-    auto rank = [](int b) { return b == SQ_PIVOT_BITS ? 0 : (b == 8 ? 1 : (b == 6 ? 2 : 3)); };
+    auto rank = [](int b) { return b == SQ_PIVOT_BITS ? 0 : 16 - b; };   // pivots, then descending width
     uint64_t off = 0;
     for (int lh = 0; lh < LH; ++lh) {
         std::vector<int> rows(dk);

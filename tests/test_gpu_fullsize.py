@@ -30,7 +30,9 @@ def _allocation(wl, seed):
     g = np.random.default_rng(seed)
     U = wl.n_units
     bits = np.full(U, min(wl.widths), np.int32)
-    if wl.budget_milli > 1000 * min(wl.widths):
+    if len(wl.widths) > 3:
+        bits = g.choice(np.asarray(wl.widths, np.int32), size=U)
+    elif wl.budget_milli > 1000 * min(wl.widths):
         bits = g.choice(np.asarray(wl.widths, np.int32), size=U, p=[0.25, 0.5, 0.25])
     piv = g.choice(U, pivot_count(wl.pivot_ppm, U), replace=False)
     bits[piv] = 16
@@ -38,7 +40,7 @@ def _allocation(wl, seed):
 
 
 FULL = [("gdn", configs.GDN_DECODE), ("kda", configs.KDA_DECODE), ("serving6", configs.SERVING_6),
-        ("outlier", configs.OUTLIER)]
+        ("outlier", configs.OUTLIER), ("outlier-mixed", configs.OUTLIER_MIXED)]
 
 
 @pytest.mark.parametrize("name,wl", FULL, ids=[c[0] for c in FULL])

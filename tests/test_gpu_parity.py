@@ -50,8 +50,9 @@ def _random_canonical(rig, seed):
 
 
 @pytest.mark.parametrize("wl,nL,B", [(configs.TINY, 1, 1), (configs.GDN_DECODE, 1, 2),
-                                     (configs.KDA_DECODE, 1, 2), (configs.OUTLIER, 1, 1)],
-                         ids=["tiny", "gdn", "kda", "outlier"])
+                                     (configs.KDA_DECODE, 1, 2), (configs.OUTLIER, 1, 1),
+                                     (configs.SERVING_4_MIXED, 2, 1), (configs.OUTLIER_MIXED, 1, 1)],
+                         ids=["tiny", "gdn", "kda", "outlier", "serving4-mixed", "outlier-mixed"])
 def test_codec_roundtrip_and_slot_isolation(torch, wl, nL, B):
     say(f"codec {wl.name} layers={nL} batch={B}")
     rig = _rig(wl, nL, B, n_slots=B + 2, slots=np.arange(B, dtype=np.int32) + 1)
@@ -71,7 +72,9 @@ def test_codec_roundtrip_and_slot_isolation(torch, wl, nL, B):
 
 
 @pytest.mark.parametrize("wl,nL,B", [(configs.GDN_DECODE, 1, 2), (configs.KDA_DECODE, 1, 1),
-                                     (configs.OUTLIER, 1, 1)], ids=["gdn", "kda", "outlier"])
+                                     (configs.OUTLIER, 1, 1), (configs.SERVING_4_MIXED, 2, 1),
+                                     (configs.OUTLIER_MIXED, 1, 1)],
+                         ids=["gdn", "kda", "outlier", "serving4-mixed", "outlier-mixed"])
 def test_unpack_is_dequantize(torch, wl, nL, B):
     say(f"unpack {wl.name}")
     rig = _rig(wl, nL, B)
@@ -88,8 +91,9 @@ def test_unpack_is_dequantize(torch, wl, nL, B):
 
 
 @pytest.mark.parametrize("wl,nL,B", [(configs.TINY, 1, 1), (configs.GDN_DECODE, 1, 2),
-                                     (configs.KDA_DECODE, 1, 2), (configs.OUTLIER, 1, 1)],
-                         ids=["tiny", "gdn", "kda", "outlier"])
+                                     (configs.KDA_DECODE, 1, 2), (configs.OUTLIER, 1, 1),
+                                     (configs.SERVING_4_MIXED, 2, 1), (configs.OUTLIER_MIXED, 1, 1)],
+                         ids=["tiny", "gdn", "kda", "outlier", "serving4-mixed", "outlier-mixed"])
 def test_pack_matches_quantize(torch, wl, nL, B):
     say(f"pack {wl.name}")
     rig = _rig(wl, nL, B)
@@ -117,6 +121,8 @@ CASES = [
     ("serving6", configs.SERVING_6, 2, 2, 3),
     ("serving4", configs.SERVING_4, 2, 2, 3),
     ("outlier", configs.OUTLIER, 1, 1, 3),
+    ("serving4-mixed", configs.SERVING_4_MIXED, 2, 2, 3),
+    ("outlier-mixed", configs.OUTLIER_MIXED, 1, 1, 3),
 ]
 
 

@@ -66,6 +66,17 @@ def test_allocation_equals_brute_force(seed, U, budget):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("seed,U,budget", [(5, 6, 4000), (6, 6, 3500), (7, 5, 5000)])
+def test_allocation_with_five_widths_equals_brute_force(seed, U, budget):
+    g = np.random.default_rng(seed)
+    widths = (2, 3, 4, 6, 8)
+    D = np.sort(g.uniform(0.01, 1.0, size=(U, 5)), axis=1)[:, ::-1] * g.uniform(1, 100, size=(U, 1))
+    got = planner.allocate(D, widths, budget)
+    assert np.array_equal(got, _brute_alloc(D, widths, budget))
+    bits = np.asarray(widths)[got]
+    assert bits.sum() * 1000 <= budget * U and len(set(bits)) > 1     # the 4-bit budget mixes widths
+
+
 def test_allocation_ties_prefer_fewer_bits():
     cost = np.zeros((4, 3))                        # distortion already zero at every width
     assert np.array_equal(planner.allocate(cost, (4, 6, 8), 8000), [0, 0, 0, 0])

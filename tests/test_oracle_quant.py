@@ -47,7 +47,7 @@ def _state(seed, N=4, dk=16, dv=12, scale=1.0):
 
 # ---------------------------------------------------------------- properties
 
-@pytest.mark.parametrize("bits", [4, 6, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
 def test_half_step_bound_and_clipping(bits):
     X = _state(1)
     rows = _rows(4, 16, bits, seed=1)
@@ -88,7 +88,7 @@ def _brute_force_fit(X, rows, r, grid):
     return out
 
 
-@pytest.mark.parametrize("dk,dv,bits", [(2, 2, 6), (4, 4, 4)])
+@pytest.mark.parametrize("dk,dv,bits", [(2, 2, 6), (4, 4, 4), (4, 4, 3), (4, 4, 2)])
 def test_column_fit_equals_brute_force(dk, dv, bits):
     X = _state(3, N=3, dk=dk, dv=dv)
     rows = _rows(3, dk, bits, seed=3)
@@ -224,7 +224,7 @@ def test_int8_comparator_matches_library_per_channel_quantization():
 
 # ---------------------------------------------------------------- per-row absmax quantizer (ablation)
 
-@pytest.mark.parametrize("bits", [4, 6, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
 def test_row_absmax_matches_library_fake_quantization(bits):
     """Per-row absmax codes = the library's per-channel symmetric quantization with the same
     (binary16-rounded) scales; the library divides in float32, so codes may differ by one

@@ -97,5 +97,11 @@ OUTLIER = Workload(
     budget_milli=4000, pivot_ppm=5000, gate_mu=3.0, gate_sigma=1.5,
     impact=("pareto", 1.5), warmup_steps=512, ridge_rows=3, ridge_cols=6, ridge_scale=20.0)
 
+# Candidate widths extended to {2, 3, 4, 6, 8}, so that a 4.0-bit budget mixes widths (the
+# pages list no candidate set; with {4, 6, 8} a 4-bit budget leaves every unit at 4 bits).
+SERVING_4_MIXED = replace(SERVING_4, name="serving-36l-32h-256req-4bit-mixed", widths=(2, 3, 4, 6, 8))
+OUTLIER_MIXED = replace(OUTLIER, name="outlier-kda-32h-128x256-mixed", widths=(2, 3, 4, 6, 8))
+
 ALL = (TINY, GDN_DECODE, KDA_DECODE, SERVING_6, SERVING_4, OUTLIER)
-BY_NAME = {w.name: w for w in ALL}
+EXTENDED = (SERVING_4_MIXED, OUTLIER_MIXED)
+BY_NAME = {w.name: w for w in ALL + EXTENDED}
