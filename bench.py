@@ -340,6 +340,29 @@ def main():
         pool4.close()
         p4.close()
         del mem4
+        # 4.0-bit budget over {2, 3, 4, 6, 8}: the planner mixes widths (calibrated like the main plan)
+        wm = configs.SERVING_4_MIXED
+        pm = sq.sq_plan_create(form=form, unit=unit, n_layers=L, n_heads=H, d_k=dk, d_v=dv, widths=wm.widths,
+                               budget_milli=wm.budget_milli, pivot_ppm=wm.pivot_ppm, grid=wm.grid,
+                               gate=gen.unit_gates(wm), impact=gen.impact_scores(wm), calib_seed=gen.calib_seed(wm),
+                               calib_segments=wm.calib_segments, calib_len=wm.calib_len)
+        memm = torch.empty(sq.sq_pool_bytes(pm, wl.n_slots), dtype=torch.uint8, device=dev)
+        poolm = sq.sq_pool_create(pm, memm, wl.n_slots)
+        Xr = torch.randn(B * H * dk * dv, device=dev)
+        for layer in range(L):
+            sq.sq_pack(poolm, layer, 1, B, slots, Xr)
+        del Xr
+        msm = time_calls(lambda: sq.sq_state_step(poolm, 0, L, B, slots, q1, k1, v1, gate, b1, y), args.steps)
+        algm = algorithmic_bytes(pm, B, sq)
+        widths_used = {str(int(w)): int(c) for w, c in zip(*np.unique(sq.sq_plan_units(pm)["unit_bits"],
+                                                                     return_counts=True))}
+        extras["budget_4bit_mixed_widths"] = {"ms": msm, "state_updates_per_s": per_step / (msm / 1e3),
+                                              "GBps": algm / (msm / 1e3) / 1e9, "algorithmic_bytes_per_launch": algm,
+                                              "compression_vs_fp32": round(pm.desc["compression_vs_fp32"], 4),
+                                              "units_per_width": widths_used}
+        poolm.close()
+        pm.close()
+        del memm
         src = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         sq.sq_copy(src, dst)
