@@ -30,7 +30,8 @@
 #include "launch.h"
 
 #ifndef STEP_WAVES_PER_EU
-#define STEP_WAVES_PER_EU 2   // minimum waves per SIMD the register allocation must allow
+#define STEP_WAVES_PER_EU 4   // waves per SIMD the register allocation targets (128 VGPRs); the spills this
+                              // costs sit in the mixed-width paths, which single-width waves never take
 #endif
 
 namespace sq {
@@ -406,6 +407,71 @@ __device__ __forceinline__ size_t e_index(const StepParams& a, int sid) {
     return (size_t)(sid / per_layer) * (size_t)a.e_layer_stride + (size_t)(sid % per_layer);
 }
 
+// Unpack + accumulate of a wave whose groups all use one code container (2, 3, 4, 6 or 8 bits):
+// straight-line code (no width branch between groups), so each group's coefficient reads and FMAs
+// stay together and the register peak stays low.
+template <int W, bool ACC, class Sh, class Smem>
+__device__ __forceinline__ void unpack_acc_uniform(uint32_t (&raw)[Sh::GPW][4], float* X, const Smem& sm, int wave,
+                                                   float* U1, float* P1, const uint8_t* rec, const uint32_t* goff,
+                                                   int lane, bool act) {
+    constexpr int CPL = Sh::CPL, GR = Sh::GR, RPW = Sh::RPW, GPW = Sh::GPW, LPR = Sh::LPR;
+#pragma unroll
+    for (int g = 0; g < GPW; ++g) {
+        float* xg = &X[16 * g];
+        if constexpr (W == 4) unpack4f(raw[g], xg);
+        else if constexpr (W == 6) unpack6f(raw[g], xg);
+        else if constexpr (W == 8) unpack8(raw[g], xg);
+        else if constexpr (W == 2) unpack2f(raw[g][0], xg);
+        else {
+            const uint32_t hi = act ? *reinterpret_cast<const uint16_t*>(rec + uniform(goff[wave * GPW + g]) +
+                                                                       LPR * 4 + lane * 2) : 0u;
+            unpack3f(raw[g][0], hi, xg);
+        }
+        if constexpr (ACC) {
+#pragma unroll
+            for (int r = 0; r < GR; ++r) {
+                const float2 cf = *reinterpret_cast<const float2*>(&sm.acc[wave * RPW + g * GR + r]);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    U1[c] = fmaf(cf.x, xg[r * CPL + c], U1[c]);
+                    P1[c] = fmaf(cf.y, xg[r * CPL + c], P1[c]);
+                }
+            }
+        }
+    }
+}
+
+// Rounding, packing and stores of a wave whose groups all use one code container.
+template <int W, class Sh, class Smem>
+__device__ __forceinline__ void round_pack_uniform(const float* X, const float* ic, const Smem& sm, uint8_t* rec,
+                                                   const uint32_t* goff, int wave, int lane, bool act) {
+    constexpr int CPL = Sh::CPL, GR = Sh::GR, RPW = Sh::RPW, GPW = Sh::GPW, LPR = Sh::LPR;
+    const float mb = kMagic + (float)bias_of(W);
+#pragma unroll
+    for (int g = 0; g < GPW; ++g) {
+        uint8_t* gp = rec + uniform(goff[wave * GPW + g]);
+        float m[16];
+        uint32_t d[4];
+#pragma unroll
+        for (int r = 0; r < GR; ++r) {
+            const float2 bd = sm.fin[wave * RPW + g * GR + r];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) m[r * CPL + c] = med3(fmaf(X[16 * g + r * CPL + c], ic[c], mb), bd.x, bd.y);
+        }
+        if constexpr (W == 4) { pack4m(m, d); if (act) store_dw<2>(gp + lane * 8, d); }
+        else if constexpr (W == 6) { pack6m(m, d); if (act) store_dw<3>(gp + lane * 12, d); }
+        else if constexpr (W == 8) { pack8m(m, d); if (act) store_dw<4>(gp + lane * 16, d); }
+        else if constexpr (W == 2) { pack2m(m, d); if (act) *reinterpret_cast<uint32_t*>(gp + lane * 4) = d[0]; }
+        else {
+            pack3m(m, d, d + 1);
+            if (act) {
+                *reinterpret_cast<uint32_t*>(gp + lane * 4) = d[0];
+                *reinterpret_cast<uint16_t*>(gp + LPR * 4 + lane * 2) = (uint16_t)d[1];
+            }
+        }
+    }
+}
+
 // One LDS round of the column fit: KG candidates c = binary16(gamma * c0), the
 // impact-weighted error F = c^2 sum_i (sqrt(w_i) r_i)^2 (t_ij / c - Q_ij)^2 of the
 // wave's rows, combined over the waves; the best candidate so far is kept (strict <).
@@ -582,6 +648,17 @@ k_state(StepParams a) {
         float U1[CPL], P1[CPL], U2[CPL], P2[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) U1[c] = P1[c] = U2[c] = P2[c] = 0.f;
+        bool same = true;
+#pragma unroll
+        for (int g = 1; g < GPW; ++g) same = same && gb[g] == gb[0];
+        if (same && gb[0] == 6) unpack_acc_uniform<6, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act);
+        else if (same && gb[0] == 4) unpack_acc_uniform<4, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act);
+        else if (same && gb[0] == 8) unpack_acc_uniform<8, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act);
+        else if (NARROW && same && gb[0] == 2)
+            unpack_acc_uniform<NARROW ? 2 : 4, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act);
+        else if (NARROW && same && gb[0] == 3)
+            unpack_acc_uniform<NARROW ? 3 : 4, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act);
+        else
 #pragma unroll
         for (int g = 0; g < GPW; ++g) {
             float* xg = &X[16 * g];
@@ -829,6 +906,15 @@ k_state(StepParams a) {
     }
 
     // ---- phase 6: round (magic-number RNE + clamp), pack and write back codes, row factors, column scales
+    bool same6 = true;
+#pragma unroll
+    for (int g = 1; g < GPW; ++g) same6 = same6 && gb[g] == gb[0];
+    if (same6 && gb[0] == 6) round_pack_uniform<6, Sh>(X, ic, sm, rec, goff, wave, lane, act);
+    else if (same6 && gb[0] == 4) round_pack_uniform<4, Sh>(X, ic, sm, rec, goff, wave, lane, act);
+    else if (same6 && gb[0] == 8) round_pack_uniform<8, Sh>(X, ic, sm, rec, goff, wave, lane, act);
+    else if (NARROW && same6 && gb[0] == 2) round_pack_uniform<NARROW ? 2 : 4, Sh>(X, ic, sm, rec, goff, wave, lane, act);
+    else if (NARROW && same6 && gb[0] == 3) round_pack_uniform<NARROW ? 3 : 4, Sh>(X, ic, sm, rec, goff, wave, lane, act);
+    else
 #pragma unroll
     for (int g = 0; g < GPW; ++g) {
         const int gg = wave * GPW + g;
