@@ -441,6 +441,23 @@ __device__ __forceinline__ void unpack_acc_uniform(uint32_t (&raw)[Sh::GPW][4], 
     }
 }
 
+// k^T D S and q^T D S partial sums of one group's rows (coefficients from LDS).
+template <bool ACC, class Sh, class Smem>
+__device__ __forceinline__ void acc_group(const Smem& sm, int wave, int g, const float* xg, float* U1, float* P1) {
+    constexpr int CPL = Sh::CPL, GR = Sh::GR, RPW = Sh::RPW;
+    if constexpr (ACC) {
+#pragma unroll
+        for (int r = 0; r < GR; ++r) {
+            const float2 cf = *reinterpret_cast<const float2*>(&sm.acc[wave * RPW + g * GR + r]);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                U1[c] = fmaf(cf.x, xg[r * CPL + c], U1[c]);
+                P1[c] = fmaf(cf.y, xg[r * CPL + c], P1[c]);
+            }
+        }
+    }
+}
+
 // Rounding, packing and stores of a wave whose groups all use one code container.
 template <int W, class Sh, class Smem>
 __device__ __forceinline__ void round_pack_uniform(const float* X, const float* ic, const Smem& sm, uint8_t* rec,
@@ -661,16 +678,19 @@ k_state(StepParams a) {
         else
 #pragma unroll
         for (int g = 0; g < GPW; ++g) {
+            // mixed widths: each branch accumulates its own group, so the compiler cannot gather the
+            // coefficient reads of every group above the branches
             float* xg = &X[16 * g];
-            if (gb[g] == 4) unpack4f(raw[g], xg);
-            else if (NARROW && gb[g] == 2) unpack2f(raw[g][0], xg);
+            if (gb[g] == 4) { unpack4f(raw[g], xg); acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1); }
+            else if (NARROW && gb[g] == 2) { unpack2f(raw[g][0], xg); acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1); }
             else if (NARROW && gb[g] == 3) {
                 const uint32_t hi = act ? *reinterpret_cast<const uint16_t*>(rec + uniform(goff[wave * GPW + g]) +
                                                                            LPR * 4 + lane * 2) : 0u;
                 unpack3f(raw[g][0], hi, xg);
+                acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1);
             }
-            else if (gb[g] == 6) unpack6f(raw[g], xg);
-            else if (gb[g] == 8) unpack8(raw[g], xg);
+            else if (gb[g] == 6) { unpack6f(raw[g], xg); acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1); }
+            else if (gb[g] == 8) { unpack8(raw[g], xg); acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1); }
             else {
                 uint32_t d16[8];
 #pragma unroll
@@ -683,18 +703,8 @@ k_state(StepParams a) {
                     const uint32_t bits = (d16[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
                     xg[e] = (sm.rb[t] == 16) ? h2f(bits) : (float)(int16_t)bits;
                 }
-            }
-            if constexpr (kAccum) {
-#pragma unroll
-                for (int r = 0; r < GR; ++r) {
-                    const float2 cf = *reinterpret_cast<const float2*>(&sm.acc[wave * RPW + g * GR + r]);
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) {
-                        U1[c] = fmaf(cf.x, xg[r * CPL + c], U1[c]);
-                        P1[c] = fmaf(cf.y, xg[r * CPL + c], P1[c]);
-                    }
-                }
-                if (gb[g] == 16) {
+                acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1);
+                if constexpr (kAccum) {
 #pragma unroll
                     for (int r = 0; r < GR; ++r) {
                         const float4 cf = sm.acc[wave * RPW + g * GR + r];
