@@ -53,6 +53,11 @@ __device__ __forceinline__ float med3(float x, float lo, float hi) {
     return __builtin_amdgcn_fmed3f(x, lo, hi);
 }
 __device__ __forceinline__ int bias_of(int bits) { return bits == 16 ? 0 : (1 << (bits - 1)); }
+// Work-group and work-item indices straight from the hardware registers.  The library's own
+// query functions are built with IEEE mode on, so with IEEE mode off here they are not inlined:
+// each kernel would call them and receive the block index in a vector register.
+__device__ __forceinline__ int block_idx() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int thread_idx() { return (int)__builtin_amdgcn_workitem_id_x(); }
 // a value every lane of the wave holds, moved to a scalar register
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
@@ -569,7 +574,7 @@ k_state(StepParams a) {
     constexpr bool kAccum = (MODE == kModeStep || MODE == kModeSplitA);
     __shared__ StepSmem<DK, DV> sm;
 
-    const int sid = blockIdx.x + a.state0;
+    const int sid = block_idx() + a.state0;
     const int h = sid % a.n_heads;
     const int b = (sid / a.n_heads) % a.batch;
     const int l = a.layer0 + sid / (a.n_heads * a.batch);
@@ -579,7 +584,7 @@ k_state(StepParams a) {
     const int slot = uniform(a.slots[b]);
     uint8_t* rec = a.pool + (uint64_t)slot * a.slot_bytes + uniform64(a.t.rec_off[lh]);
     uint16_t* rs = reinterpret_cast<uint16_t*>(rec + uniform(a.t.scale_off[lh]));   // row factors, then column scales
-    const int tid = threadIdx.x, wave = uniform(threadIdx.x >> 6), lane = tid & 63;
+    const int tid = thread_idx(), wave = uniform(tid >> 6), lane = tid & 63;
     const bool act = lane < LPR;
     const int col0 = lane * CPL;
     const uint8_t* gbits = a.t.grp_bits + (size_t)lh * NG;
@@ -980,14 +985,14 @@ __global__ void __launch_bounds__(nw_of(DK, DV) * 64)
 k_codec(CodecParams a) {
     using Sh = Shape<DK, DV>;
     constexpr int CPL = Sh::CPL, LPR = Sh::LPR, RPW = Sh::RPW, GPW = Sh::GPW, NG = Sh::NG;
-    const int sid = blockIdx.x;
+    const int sid = block_idx();
     const int h = sid % a.n_heads;
     const int b = (sid / a.n_heads) % a.batch;
     const int l = a.layer0 + sid / (a.n_heads * a.batch);
     const int lh = l * a.n_heads + h;
     uint8_t* rec = a.pool + (uint64_t)a.slots[b] * a.slot_bytes + a.t.rec_off[lh];
     uint16_t* rs = reinterpret_cast<uint16_t*>(rec + a.t.scale_off[lh]);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = thread_idx(), wave = tid >> 6, lane = tid & 63;
     const int col0 = lane * CPL;
     const uint16_t* perm = a.t.perm + (size_t)lh * DK;
     const uint8_t* rbits = a.t.row_bits + (size_t)lh * DK;
@@ -1060,7 +1065,7 @@ k_codec(CodecParams a) {
         if constexpr (EXPORT) a.r[(size_t)sid * DK + i] = rs[tid];
         else rs[tid] = a.r[(size_t)sid * DK + i];
     }
-    for (int j = tid; j < DV; j += blockDim.x) {
+    for (int j = tid; j < DV; j += nw_of(DK, DV) * 64) {
         if constexpr (EXPORT) a.c[(size_t)sid * DV + j] = rs[DK + j];
         else rs[DK + j] = a.c[(size_t)sid * DV + j];
     }
@@ -1125,12 +1130,12 @@ k_cmp(CmpParams a) {
     __shared__ float s_ck[DK], s_cq[DK], s_al[DK], s_bk[DK], s_sc[DK];
     __shared__ float s_part[NW][2][DV];
     __shared__ float s_red[NW];
-    const int sid = blockIdx.x;
+    const int sid = block_idx();
     const int h = sid % a.n_heads;
     const int b = (sid / a.n_heads) % a.batch;
     const int ll = sid / (a.n_heads * a.batch);
     const size_t st = ((size_t)(a.layer0 + ll) * a.n_slots + a.slots[b]) * a.n_heads + h;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = thread_idx(), wave = tid >> 6, lane = tid & 63;
     const bool act = lane < LPR;
     const int col0 = lane * CPL;
     float kq = 0.f;
@@ -1236,9 +1241,10 @@ k_cmp(CmpParams a) {
     }
 }
 
-__global__ void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+constexpr int kCopyThreads = 256;
+__global__ void __launch_bounds__(kCopyThreads)
+k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n, size_t stride) {
+    for (size_t i = (size_t)block_idx() * kCopyThreads + thread_idx(); i < n; i += stride) dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1333,10 +1339,10 @@ hipError_t launch_cmp(int dk, int dv, bool int8, int form, int n_heads, int n_sl
 hipError_t launch_copy(const void* src, void* dst, size_t n_bytes, hipStream_t s) {
     const size_t n = n_bytes / 16;
     if (n == 0) return hipSuccess;
-    const int threads = 256;
-    size_t blocks = (n + threads - 1) / threads;
+    size_t blocks = (n + kCopyThreads - 1) / kCopyThreads;
     if (blocks > 256 * 32) blocks = 256 * 32;
-    k_copy<<<dim3((unsigned)blocks), dim3(threads), 0, s>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst), n);
+    k_copy<<<dim3((unsigned)blocks), dim3(kCopyThreads), 0, s>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst), n,
+                                                                 blocks * kCopyThreads);
     return hipGetLastError();
 }
 
