@@ -526,17 +526,36 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
         }
         const float4 f = sm.fit[wave * RPW + r];
         const float qm = f.w, sw = f.y;
+        // The error is odd in t and round-half-even is symmetric, so the fit works on |t| (a free
+        // source modifier) and the clamp is one v_min.  The row's KG x CPL chains advance in stages
+        // separated by empty asm statements: left alone, the scheduler runs each chain to its end
+        // before the next, and a wave then stalls on every dependent step.
+        float t[CPL], R[KG][CPL], E[KG][CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const float t = X[r * CPL + c];
+        for (int c = 0; c < CPL; ++c) t[c] = fabsf(X[r * CPL + c]);
 #pragma unroll
-            for (int j = 0; j < KG; ++j) {
-                const float R = rintf(t * icg[j][c]);
-                const float Qc = (FREE0 && j == 0) ? R : med3(R, -qm, qm);
-                const float dd = sw * fmaf(t, icg[j][c], -Qc);
-                Fp[j][c] = fmaf(dd, dd, Fp[j][c]);
+        for (int j = 0; j < KG; ++j)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) R[j][c] = rintf(t[c] * icg[j][c]);
+#pragma unroll
+        for (int j = 0; j < KG; ++j)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) __asm__ volatile("" : "+v"(R[j][c]));
+#pragma unroll
+        for (int j = 0; j < KG; ++j)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const float Qc = (FREE0 && j == 0) ? R[j][c] : fminf(R[j][c], qm);
+                E[j][c] = sw * fmaf(t[c], icg[j][c], -Qc);
             }
-        }
+#pragma unroll
+        for (int j = 0; j < KG; ++j)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) __asm__ volatile("" : "+v"(E[j][c]));
+#pragma unroll
+        for (int j = 0; j < KG; ++j)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) Fp[j][c] = fmaf(E[j][c], E[j][c], Fp[j][c]);
     }
     if (act) {
 #pragma unroll
