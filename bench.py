@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the comparators (INT8 per-row, FP32), the split arrangement, the candidate-grid "
-                         "sweep, the 4-bit budget and the copy reference")
+                         "sweep, the 4-bit budgets, the copy reference and the dual-axis outlier pool")
     return ap.parse_args()
 
 
@@ -151,6 +151,80 @@ def cpu_baseline(wl, seconds):
             "sample": f"{done} state updates over {cores} processes (each 64 sampled (layer, head) states of the "
                       f"workload with 6-bit rows, steps repeated for {2 * seconds / 3:.0f} s) plus {n1} in one "
                       f"thread, by the float64 NumPy oracle, BLAS limited to one thread per process"}
+
+
+def outlier_comparison(sq, torch, dev, steps):
+    """The dual-axis outlier pool (KDA, 128x256 states, 1024 requests x 32 heads, per-row widths at a 4.0-bit
+    budget with FP16 pivot rows) against the uniform INT8 per-row and FP32 states on the same state and inputs.
+    The state is Gaussian with each head's ridge rows and columns scaled as in the workload's warm-up; the v of
+    each step carries the ridge columns."""
+    import numpy as np
+    from workloads import configs, gen
+    wl = configs.OUTLIER
+    L, H, dk, dv, B = wl.n_layers, wl.n_heads, wl.d_k, wl.d_v, wl.batch
+    n = L * B * H
+    t0 = time.perf_counter()
+    plan = sq.sq_plan_create(form=sq.SQ_FORM_KDA, unit=sq.SQ_UNIT_ROW, n_layers=L, n_heads=H, d_k=dk, d_v=dv,
+                             widths=wl.widths, budget_milli=wl.budget_milli, pivot_ppm=wl.pivot_ppm, grid=wl.grid,
+                             gate=gen.unit_gates(wl), impact=gen.impact_scores(wl), calib_seed=gen.calib_seed(wl),
+                             calib_segments=wl.calib_segments, calib_len=wl.calib_len)
+    log(f"outlier plan: {time.perf_counter() - t0:.1f} s")
+    mem = torch.empty(sq.sq_pool_bytes(plan, wl.n_slots), dtype=torch.uint8, device=dev)
+    pool = sq.sq_pool_create(plan, mem, wl.n_slots)
+    slots = torch.tensor(gen.slot_map(wl), dtype=torch.int32, device=dev)
+    ident = torch.arange(B, dtype=torch.int32, device=dev)
+    rows, cols = gen.ridge_positions(wl)                                 # [L, H, r], [L, H, c]
+    rscale = torch.ones(H, dk, device=dev)
+    cscale = torch.ones(H, dv, device=dev)
+    for h in range(H):
+        rscale[h, torch.as_tensor(rows[0, h], device=dev)] = wl.ridge_scale
+        cscale[h, torch.as_tensor(cols[0, h], device=dev)] = wl.ridge_scale
+    g = torch.Generator(device=dev)
+    g.manual_seed(41)
+    S = torch.randn(B, H, dk, dv, device=dev, generator=g)
+    S *= rscale[None, :, :, None]
+    S *= cscale[None, :, None, :]
+    S = S.reshape(-1)
+    sq.sq_pack(pool, 0, L, B, slots, S)
+    q = torch.randn(n, dk, device=dev, generator=g)
+    k = torch.randn(n, dk, device=dev, generator=g)
+    q = (q / q.norm(dim=1, keepdim=True)).reshape(-1).contiguous()
+    k = (k / k.norm(dim=1, keepdim=True)).reshape(-1).contiguous()
+    v = (torch.randn(B, H, dv, device=dev, generator=g) * cscale[None]).reshape(-1).contiguous()
+    beta = torch.sigmoid(torch.randn(n, device=dev, generator=g))
+    gate = torch.tensor(gen.unit_gates(wl), device=dev)[:, None].expand(L, B, H, dk).contiguous().reshape(-1)
+    y = torch.empty(n * dv, device=dev)
+    ms_q = time_calls(lambda: sq.sq_state_step(pool, 0, L, B, slots, q, k, v, gate, beta, y), steps)
+    alg = algorithmic_bytes(plan, B, sq)
+    out = {"workload": wl.name, "states_per_step": n,
+           "packed_4bit": {"ms": ms_q, "state_updates_per_s": n / (ms_q / 1e3), "GBps": alg / (ms_q / 1e3) / 1e9,
+                           "algorithmic_bytes_per_launch": alg,
+                           "compression_vs_fp32": round(plan.desc["compression_vs_fp32"], 4)}}
+    pool.close()
+    plan.close()
+    del mem
+    codes8 = torch.empty(n * dk * dv, dtype=torch.int8, device=dev)
+    scales8 = torch.empty(n * dk, dtype=torch.float32, device=dev)
+    Sv, Cv, Rv = S.view(n, dk, dv), codes8.view(n, dk, dv), scales8.view(n, dk)
+    for i0 in range(0, n, 4096):
+        blk = Sv[i0:i0 + 4096]
+        sc = (blk.abs().amax(dim=2) / 127.0).clamp_min(1e-30)
+        Rv[i0:i0 + 4096] = sc
+        Cv[i0:i0 + 4096] = torch.clamp(torch.round(blk / sc[:, :, None]), -127, 127).to(torch.int8)
+    ms8 = time_calls(lambda: sq.sq_int8_step(sq.SQ_FORM_KDA, H, dk, dv, B, 0, L, B, ident, codes8, scales8, q, k, v,
+                                             gate, beta, y), steps)
+    by8 = per_state_bytes(dk, dv, 1, dk * dv + 4 * dk)
+    out["int8_row"] = {"ms": ms8, "state_updates_per_s": n / (ms8 / 1e3), "GBps": n * by8 / (ms8 / 1e3) / 1e9,
+                       "state_bytes": dk * dv + 4 * dk}
+    del codes8, scales8, Sv, Cv, Rv
+    ms32 = time_calls(lambda: sq.sq_fp32_step(sq.SQ_FORM_KDA, H, dk, dv, B, 0, L, B, ident, S, q, k, v, gate, beta,
+                                              y), steps)
+    by32 = per_state_bytes(dk, dv, 1, 4 * dk * dv)
+    out["fp32"] = {"ms": ms32, "state_updates_per_s": n / (ms32 / 1e3), "GBps": n * by32 / (ms32 / 1e3) / 1e9,
+                   "state_bytes": 4 * dk * dv}
+    del S
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -376,6 +450,8 @@ def main():
         extras["copy_reference"] = {"bytes_moved": 2 * src.numel(), "ms": cms,
                                     "GBps": 2 * src.numel() / cms / 1e6}
         del src, dst
+        torch.cuda.empty_cache()
+        extras["outlier_dual_axis"] = outlier_comparison(sq, torch, dev, args.steps)
         out["extras"] = extras
     if cpu is not None:
         out["cpu_baseline"] = cpu

@@ -1288,12 +1288,13 @@ static hipError_t launch_state_kg(int mode, const StepParams& p, int n_states, h
                     : launch_state_kgn<DK, DV, KG, false>(mode, p, n_states, s);
 }
 
-// candidates per LDS round: one or two when the grid is that small, otherwise four
-// (a last round with fewer candidates repeats the final one, which cannot change the choice)
+// candidates per LDS round: one or two when the grid is that small, otherwise four; two for
+// four columns per lane (d_v = 256), where four would spill (a last round with fewer candidates
+// repeats the final one, which cannot change the choice)
 template <int DK, int DV>
 static hipError_t launch_state_t(int mode, const StepParams& p, int n_states, hipStream_t s) {
     if (p.n_grid == 1) return launch_state_kg<DK, DV, 1>(mode, p, n_states, s);
-    if (p.n_grid == 2) return launch_state_kg<DK, DV, 2>(mode, p, n_states, s);
+    if (p.n_grid == 2 || Shape<DK, DV>::CPL > 2) return launch_state_kg<DK, DV, 2>(mode, p, n_states, s);
     return launch_state_kg<DK, DV, 4>(mode, p, n_states, s);
 }
 
