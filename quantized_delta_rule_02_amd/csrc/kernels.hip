@@ -30,8 +30,8 @@
 #include "launch.h"
 
 #ifndef STEP_WAVES_PER_EU
-#define STEP_WAVES_PER_EU 4   // waves per SIMD the register allocation targets (128 VGPRs); the spills this
-                              // costs sit in the mixed-width paths, which single-width waves never take
+#define STEP_WAVES_PER_EU 4   // waves per SIMD the register allocation targets (128 VGPRs; the 128x128
+                              // step fits without spills)
 #endif
 
 namespace sq {

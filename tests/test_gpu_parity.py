@@ -51,8 +51,9 @@ def _random_canonical(rig, seed):
 
 @pytest.mark.parametrize("wl,nL,B", [(configs.TINY, 1, 1), (configs.GDN_DECODE, 1, 2),
                                      (configs.KDA_DECODE, 1, 2), (configs.OUTLIER, 1, 1),
-                                     (configs.SERVING_4_MIXED, 2, 1), (configs.OUTLIER_MIXED, 1, 1)],
-                         ids=["tiny", "gdn", "kda", "outlier", "serving4-mixed", "outlier-mixed"])
+                                     (configs.SERVING_4_MIXED, 2, 1), (configs.OUTLIER_MIXED, 1, 1),
+                                     (configs.GDN_64, 1, 2)],
+                         ids=["tiny", "gdn", "kda", "outlier", "serving4-mixed", "outlier-mixed", "gdn64"])
 def test_codec_roundtrip_and_slot_isolation(torch, wl, nL, B):
     say(f"codec {wl.name} layers={nL} batch={B}")
     rig = _rig(wl, nL, B, n_slots=B + 2, slots=np.arange(B, dtype=np.int32) + 1)
@@ -73,8 +74,8 @@ def test_codec_roundtrip_and_slot_isolation(torch, wl, nL, B):
 
 @pytest.mark.parametrize("wl,nL,B", [(configs.GDN_DECODE, 1, 2), (configs.KDA_DECODE, 1, 1),
                                      (configs.OUTLIER, 1, 1), (configs.SERVING_4_MIXED, 2, 1),
-                                     (configs.OUTLIER_MIXED, 1, 1)],
-                         ids=["gdn", "kda", "outlier", "serving4-mixed", "outlier-mixed"])
+                                     (configs.OUTLIER_MIXED, 1, 1), (configs.KDA_64, 1, 2)],
+                         ids=["gdn", "kda", "outlier", "serving4-mixed", "outlier-mixed", "kda64"])
 def test_unpack_is_dequantize(torch, wl, nL, B):
     say(f"unpack {wl.name}")
     rig = _rig(wl, nL, B)
@@ -92,8 +93,9 @@ def test_unpack_is_dequantize(torch, wl, nL, B):
 
 @pytest.mark.parametrize("wl,nL,B", [(configs.TINY, 1, 1), (configs.GDN_DECODE, 1, 2),
                                      (configs.KDA_DECODE, 1, 2), (configs.OUTLIER, 1, 1),
-                                     (configs.SERVING_4_MIXED, 2, 1), (configs.OUTLIER_MIXED, 1, 1)],
-                         ids=["tiny", "gdn", "kda", "outlier", "serving4-mixed", "outlier-mixed"])
+                                     (configs.SERVING_4_MIXED, 2, 1), (configs.OUTLIER_MIXED, 1, 1),
+                                     (configs.GDN_64, 1, 2), (configs.KDA_64, 1, 2)],
+                         ids=["tiny", "gdn", "kda", "outlier", "serving4-mixed", "outlier-mixed", "gdn64", "kda64"])
 def test_pack_matches_quantize(torch, wl, nL, B):
     say(f"pack {wl.name}")
     rig = _rig(wl, nL, B)
@@ -123,6 +125,8 @@ CASES = [
     ("outlier", configs.OUTLIER, 1, 1, 3),
     ("serving4-mixed", configs.SERVING_4_MIXED, 2, 2, 3),
     ("outlier-mixed", configs.OUTLIER_MIXED, 1, 1, 3),
+    ("gdn64", configs.GDN_64, 1, 2, 4),
+    ("kda64", configs.KDA_64, 1, 2, 4),
 ]
 
 

@@ -57,7 +57,8 @@ CASES = [("tiny", configs.TINY, 1, 2, 16, 0), ("gdn", configs.GDN_DECODE, 1, 2, 
          ("kda", configs.KDA_DECODE, 1, 2, 16, 0), ("serving", configs.SERVING_6, 2, 1, 16, 0),
          ("outlier", configs.OUTLIER, 1, 1, 12, 0), ("gdn-row-absmax", configs.GDN_DECODE, 1, 2, 24, 1),
          ("kda-row-absmax", configs.KDA_DECODE, 1, 2, 16, 1),
-         ("serving4-mixed", configs.SERVING_4_MIXED, 2, 1, 16, 0), ("outlier-mixed", configs.OUTLIER_MIXED, 1, 1, 12, 0)]
+         ("serving4-mixed", configs.SERVING_4_MIXED, 2, 1, 16, 0), ("outlier-mixed", configs.OUTLIER_MIXED, 1, 1, 12, 0),
+         ("kda64", configs.KDA_64, 1, 2, 16, 0)]
 
 
 @pytest.mark.parametrize("name,wl,nL,S,T,qz", CASES, ids=[c[0] for c in CASES])

@@ -102,6 +102,10 @@ OUTLIER = Workload(
 SERVING_4_MIXED = replace(SERVING_4, name="serving-36l-32h-256req-4bit-mixed", widths=(2, 3, 4, 6, 8))
 OUTLIER_MIXED = replace(OUTLIER, name="outlier-kda-32h-128x256-mixed", widths=(2, 3, 4, 6, 8))
 
+# The 64x64 state shape (one wave per state in the library): test cases only.
+GDN_64 = replace(GDN_DECODE, name="gdn-decode-32h-64", d_k=64, d_v=64)
+KDA_64 = replace(KDA_DECODE, name="kda-decode-32h-64", d_k=64, d_v=64)
+
 ALL = (TINY, GDN_DECODE, KDA_DECODE, SERVING_6, SERVING_4, OUTLIER)
-EXTENDED = (SERVING_4_MIXED, OUTLIER_MIXED)
+EXTENDED = (SERVING_4_MIXED, OUTLIER_MIXED, GDN_64, KDA_64)
 BY_NAME = {w.name: w for w in ALL + EXTENDED}
