@@ -26,6 +26,8 @@
  *     current device); "h_" or unprefixed pointers in sq_plan_cfg are host.
  *   - Streams are passed as void* and hold a hipStream_t (NULL = the null stream).
  *   - Per-step arrays are laid out [n_layers][batch][H][d] (row-major, fp32).
+ *   - A call over an empty range (batch = 0 or n_layers = 0) validates its
+ *     sizes and returns SQ_OK without touching any array (they may be NULL).
  *   - Every call validates its arguments on the host before enqueuing work and
  *     returns a negative sq_status on failure, with a message available from
  *     sq_last_error() on the calling thread.  Device work is asynchronous: a

@@ -369,7 +369,7 @@ extern "C" sq_status sq_pool_create(const sq_plan* p, void* d_pool, size_t pool_
 
 static sq_status check_range(const sq_pool* pl, int32_t layer0, int32_t n_layers, int32_t batch) {
     if (!pl) { set_error("pool is NULL"); return SQ_ERR_ARG; }
-    if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > pl->L) {
+    if (layer0 < 0 || n_layers < 0 || layer0 + n_layers > pl->L) {
         set_error("layers [%d, %d) outside the plan's %d layers", layer0, layer0 + n_layers, pl->L);
         return SQ_ERR_PLAN_MISMATCH;
     }
@@ -420,7 +420,7 @@ extern "C" sq_status sq_state_step(sq_pool* pl, int32_t layer0, int32_t n_layers
     sq_status st = check_range(pl, layer0, n_layers, batch);
     if (st != SQ_OK) return st;
     if (flags & ~(SQ_STEP_SPLIT | SQ_STEP_VALIDATE | SQ_STEP_NO_JOIN)) { set_error("unknown flags 0x%x", flags); return SQ_ERR_ARG; }
-    if (batch == 0) return SQ_OK;
+    if (batch == 0 || n_layers == 0) return SQ_OK;   // nothing to do
     if (!d_slots || !d_q || !d_k || !d_v || !d_gate || !d_beta || !d_y) { set_error("NULL device array"); return SQ_ERR_ARG; }
     hipStream_t sm = static_cast<hipStream_t>(stream_main);
     hipStream_t sa = stream_aux ? static_cast<hipStream_t>(stream_aux) : sm;
@@ -491,7 +491,7 @@ extern "C" sq_status sq_pack(sq_pool* pl, int32_t layer0, int32_t n_layers, int3
                              const float* d_X, void* stream) {
     sq_status st = check_range(pl, layer0, n_layers, batch);
     if (st != SQ_OK) return st;
-    if (batch == 0) return SQ_OK;
+    if (batch == 0 || n_layers == 0) return SQ_OK;   // nothing to do
     if (!d_slots || !d_X) { set_error("NULL device array"); return SQ_ERR_ARG; }
     StepParams p = base_params(pl, layer0, n_layers, batch, d_slots);
     p.x_in = d_X;
@@ -503,7 +503,7 @@ extern "C" sq_status sq_unpack(sq_pool* pl, int32_t layer0, int32_t n_layers, in
                                float* d_X, void* stream) {
     sq_status st = check_range(pl, layer0, n_layers, batch);
     if (st != SQ_OK) return st;
-    if (batch == 0) return SQ_OK;
+    if (batch == 0 || n_layers == 0) return SQ_OK;   // nothing to do
     if (!d_slots || !d_X) { set_error("NULL device array"); return SQ_ERR_ARG; }
     StepParams p = base_params(pl, layer0, n_layers, batch, d_slots);
     p.x_out = d_X;
@@ -515,7 +515,7 @@ static sq_status codec(sq_pool* pl, bool do_export, int32_t layer0, int32_t n_la
                        const int32_t* d_slots, int16_t* codes, uint16_t* r, uint16_t* c, void* stream) {
     sq_status st = check_range(pl, layer0, n_layers, batch);
     if (st != SQ_OK) return st;
-    if (batch == 0) return SQ_OK;
+    if (batch == 0 || n_layers == 0) return SQ_OK;   // nothing to do
     if (!d_slots || !codes || !r || !c) { set_error("NULL device array"); return SQ_ERR_ARG; }
     CodecParams p{};
     p.pool = pl->pool; p.slot_bytes = pl->slot_bytes; p.t = pl->t; p.n_heads = pl->H; p.layer0 = layer0;
@@ -543,12 +543,12 @@ static sq_status cmp_step(bool int8, int32_t form, int32_t H, int32_t dk, int32_
                           float* y, void* stream) {
     if (form != SQ_FORM_GDN && form != SQ_FORM_KDA) { set_error("form %d", form); return SQ_ERR_ARG; }
     if (!shape_supported(dk, dv)) { set_error("state shape %dx%d is not compiled in", dk, dv); return SQ_ERR_UNSUPPORTED; }
-    if (H < 1 || n_slots < 1 || layer0 < 0 || n_layers < 1 || batch < 0 || batch > n_slots) {
+    if (H < 1 || n_slots < 1 || layer0 < 0 || n_layers < 0 || batch < 0 || batch > n_slots) {
         set_error("bad sizes");
         return SQ_ERR_ARG;
     }
     if (int64_t(n_layers) * batch * H > int64_t(0x7FFFFFFF)) { set_error("too many states in one call"); return SQ_ERR_ARG; }
-    if (batch == 0) return SQ_OK;
+    if (batch == 0 || n_layers == 0) return SQ_OK;   // nothing to do
     if (!slots || !q || !k || !v || !gate || !beta || !y || (int8 ? (!codes || !scales) : !S)) {
         set_error("NULL device array");
         return SQ_ERR_ARG;

@@ -282,7 +282,7 @@ struct Shape {
 template <int DK, int DV>
 struct StepSmem {
     float4 acc[DK];    // column accumulation: A k, A q (code rows), alpha k, alpha q (pivot rows)
-    float4 upd[DK];    // update: A = alpha r_old, -A * bias, beta k, alpha (pivot rows)
+    float4 upd[DK];    // update: A = alpha r_old (code rows), beta k, alpha (pivot rows), unused
     float4 fit[DK];    // requantization: 1 / r_new, sqrt(w) r_new, 1 / qmax, qmax
     float2 fin[DK];    // final rounding bounds: magic + container bias -/+ qmax
     float rn[DK];      // new binary16 row factor
@@ -302,7 +302,7 @@ __device__ __forceinline__ uint32_t gather4(uint32_t r0, uint32_t r1, uint32_t r
     return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 
-// fast unpack of one lane's 16 biased codes to float (layout in internal.h)
+// fast unpack of one lane's 16 stored (offset) codes to float (layout in internal.h)
 __device__ __forceinline__ void unpack4f(const uint32_t* d, float* o) {
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
@@ -412,13 +412,24 @@ __device__ __forceinline__ size_t e_index(const StepParams& a, int sid) {
     return (size_t)(sid / per_layer) * (size_t)a.e_layer_stride + (size_t)(sid % per_layer);
 }
 
+// Stored codes carry the container's offset 2^(W-1).  One FMA per entry turns a stored code into
+// c_j Q_ij (exact: an 11-bit scale times a code of at most 8 bits), which the column sums and the
+// update then use.  Summing offset codes and taking the offset's sum off afterwards would lose the
+// cancellation to rounding: for a state whose stored scales are large next to its new values (a zero
+// state keeps r = c = 1) the lost digits reach the rounding of the new codes.
+template <int CPL>
+__device__ __forceinline__ void scale_codes(float* xg, const float* c_old, float bias) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xg[e] = fmaf(xg[e], c_old[e % CPL], -bias * c_old[e % CPL]);
+}
+
 // Unpack + accumulate of a wave whose groups all use one code container (2, 3, 4, 6 or 8 bits):
 // straight-line code (no width branch between groups), so each group's coefficient reads and FMAs
 // stay together and the register peak stays low.
 template <int W, bool ACC, class Sh, class Smem>
 __device__ __forceinline__ void unpack_acc_uniform(uint32_t (&raw)[Sh::GPW][4], float* X, const Smem& sm, int wave,
                                                    float* U1, float* P1, const uint8_t* rec, const uint32_t* goff,
-                                                   int lane, bool act) {
+                                                   int lane, bool act, const float* c_old) {
     constexpr int CPL = Sh::CPL, GR = Sh::GR, RPW = Sh::RPW, GPW = Sh::GPW, LPR = Sh::LPR;
 #pragma unroll
     for (int g = 0; g < GPW; ++g) {
@@ -432,6 +443,7 @@ __device__ __forceinline__ void unpack_acc_uniform(uint32_t (&raw)[Sh::GPW][4], 
                                                                        LPR * 4 + lane * 2) : 0u;
             unpack3f(raw[g][0], hi, xg);
         }
+        scale_codes<CPL>(xg, c_old, (float)(1 << (W - 1)));
         if constexpr (ACC) {
 #pragma unroll
             for (int r = 0; r < GR; ++r) {
@@ -636,11 +648,10 @@ k_state(StepParams a) {
     }
 
     // ---- phase 0: per-row coefficients of this wave's rows (lane r < RPW takes row wave * RPW + r)
-    float kq_part = 0.f, kb_part = 0.f, qb_part = 0.f;
+    float kq_part = 0.f;
     if (lane < RPW) {
         const int t = wave * RPW + lane;
         const int rbits = a.t.row_bits[(size_t)lh * DK + t];
-        const int sb = gbits[t / GR];
         const bool piv = rbits == 16;
         sm.rb[t] = rbits;
         sm.w[t] = a.t.row_w[(size_t)lh * DK + t];
@@ -655,29 +666,20 @@ k_state(StepParams a) {
                 bt = a.beta[sid];
             }
             const float A = piv ? 0.f : al * rold;
-            const float bias = (float)bias_of(sb);
             sm.acc[t] = make_float4(A * kk, A * qq, piv ? al * kk : 0.f, piv ? al * qq : 0.f);
-            sm.upd[t] = make_float4(A, -A * bias, bt * kk, piv ? al : 0.f);
+            sm.upd[t] = make_float4(A, bt * kk, piv ? al : 0.f, 0.f);
             kq_part = kk * qq;
-            kb_part = A * kk * bias;
-            qb_part = A * qq * bias;
         }
     }
     if constexpr (kAccum) {
         kq_part = wave_sum(kq_part);
-        kb_part = wave_sum(kb_part);
-        qb_part = wave_sum(qb_part);
-        if (lane == 0) {
-            sm.red[wave][0] = kq_part;
-            sm.red[wave][1] = kb_part;
-            sm.red[wave][2] = qb_part;
-        }
+        if (lane == 0) sm.red[wave][0] = kq_part;
     }
     wave_lds_sync();
 
     float X[EPL];
 
-    // ---- phase 1: unpack (biased codes / pivot values), column accumulations k^T D S, q^T D S
+    // ---- phase 1: unpack (signed codes / pivot values), column accumulations k^T D S, q^T D S
     if constexpr (MODE == kModePack) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -692,29 +694,46 @@ k_state(StepParams a) {
         bool same = true;
 #pragma unroll
         for (int g = 1; g < GPW; ++g) same = same && gb[g] == gb[0];
-        if (same && gb[0] == 6) unpack_acc_uniform<6, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act);
-        else if (same && gb[0] == 4) unpack_acc_uniform<4, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act);
-        else if (same && gb[0] == 8) unpack_acc_uniform<8, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act);
+        if (same && gb[0] == 6) unpack_acc_uniform<6, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act, c_old);
+        else if (same && gb[0] == 4) unpack_acc_uniform<4, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act, c_old);
+        else if (same && gb[0] == 8) unpack_acc_uniform<8, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act, c_old);
         else if (NARROW && same && gb[0] == 2)
-            unpack_acc_uniform<NARROW ? 2 : 4, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act);
+            unpack_acc_uniform<NARROW ? 2 : 4, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act, c_old);
         else if (NARROW && same && gb[0] == 3)
-            unpack_acc_uniform<NARROW ? 3 : 4, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act);
+            unpack_acc_uniform<NARROW ? 3 : 4, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act, c_old);
         else
 #pragma unroll
         for (int g = 0; g < GPW; ++g) {
             // mixed widths: each branch accumulates its own group, so the compiler cannot gather the
             // coefficient reads of every group above the branches
             float* xg = &X[16 * g];
-            if (gb[g] == 4) { unpack4f(raw[g], xg); acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1); }
-            else if (NARROW && gb[g] == 2) { unpack2f(raw[g][0], xg); acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1); }
+            if (gb[g] == 4) {
+                unpack4f(raw[g], xg);
+                scale_codes<CPL>(xg, c_old, 8.f);
+                acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1);
+            }
+            else if (NARROW && gb[g] == 2) {
+                unpack2f(raw[g][0], xg);
+                scale_codes<CPL>(xg, c_old, 2.f);
+                acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1);
+            }
             else if (NARROW && gb[g] == 3) {
                 const uint32_t hi = act ? *reinterpret_cast<const uint16_t*>(rec + uniform(goff[wave * GPW + g]) +
                                                                            LPR * 4 + lane * 2) : 0u;
                 unpack3f(raw[g][0], hi, xg);
+                scale_codes<CPL>(xg, c_old, 4.f);
                 acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1);
             }
-            else if (gb[g] == 6) { unpack6f(raw[g], xg); acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1); }
-            else if (gb[g] == 8) { unpack8(raw[g], xg); acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1); }
+            else if (gb[g] == 6) {
+                unpack6f(raw[g], xg);
+                scale_codes<CPL>(xg, c_old, 32.f);
+                acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1);
+            }
+            else if (gb[g] == 8) {
+                unpack8(raw[g], xg);
+                scale_codes<CPL>(xg, c_old, 128.f);
+                acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1);
+            }
             else {
                 uint32_t d16[8];
 #pragma unroll
@@ -725,7 +744,7 @@ k_state(StepParams a) {
                 for (int e = 0; e < 16; ++e) {
                     const int t = wave * RPW + (16 * g + e) / CPL;
                     const uint32_t bits = (d16[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                    xg[e] = (sm.rb[t] == 16) ? h2f(bits) : (float)(int16_t)bits;
+                    xg[e] = (sm.rb[t] == 16) ? h2f(bits) : c_old[e % CPL] * (float)(int16_t)bits;
                 }
                 acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1);
                 if constexpr (kAccum) {
@@ -750,7 +769,7 @@ k_state(StepParams a) {
                 const int c = e % CPL;
                 const float4 u = sm.upd[t];
                 const bool piv = sm.rb[t] == 16;
-                const float s = piv ? X[e] : c_old[c] * fmaf(u.x, X[e], u.y);
+                const float s = piv ? X[e] : u.x * X[e];
                 const int i = a.t.perm[(size_t)lh * DK + t];
                 if (act) a.x_out[((size_t)sid * DK + i) * DV + col0 + c] = s;
             }
@@ -769,13 +788,9 @@ k_state(StepParams a) {
                 }
             }
             __syncthreads();
-            float kq = 0.f, kb = 0.f, qb = 0.f;
+            float kq = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                kq += sm.red[w][0];
-                kb += sm.red[w][1];
-                qb += sm.red[w][2];
-            }
+            for (int w = 0; w < NW; ++w) kq += sm.red[w][0];
             const float bt = a.beta[sid];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
@@ -789,8 +804,8 @@ k_state(StepParams a) {
                         sp2 += sm.part[w][3][col0 + c];
                     }
                 }
-                const float u = fmaf(c_old[c], su - kb, su2);      // k^T D S
-                const float p = fmaf(c_old[c], sp - qb, sp2);      // q^T D S
+                const float u = su + su2;      // k^T D S
+                const float p = sp + sp2;      // q^T D S
                 const float e = act ? a.v[(size_t)sid * DV + col0 + c] - u : 0.f;
                 ecol[c] = e;
                 if (act && wave == 0) a.y[(size_t)sid * DV + col0 + c] = fmaf(bt * kq, e, p);
@@ -815,7 +830,7 @@ k_state(StepParams a) {
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
                         const int e = 16 * g + r * CPL + c;
-                        X[e] = fmaf(c_old[c], fmaf(u.x, X[e], u.y), u.z * ecol[c]);
+                        X[e] = fmaf(u.x, X[e], u.y * ecol[c]);
                     }
                 }
             } else {
@@ -827,8 +842,8 @@ k_state(StepParams a) {
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
                         const int e = 16 * g + r * CPL + c;
-                        const float dq = piv ? u.w * X[e] : c_old[c] * (u.x * X[e]);
-                        X[e] = fmaf(u.z, ecol[c], dq);
+                        const float dq = (piv ? u.z : u.x) * X[e];
+                        X[e] = fmaf(u.y, ecol[c], dq);
                     }
                 }
             }

@@ -47,15 +47,16 @@ def from_canonical(codes, r, c, rows: quant.RowPlan) -> quant.Packed:
                         c=fp16_from_bits(np.asarray(c).view(np.uint16)), V=V)
 
 
-def step_error_bound(P0: quant.Packed, rows: quant.RowPlan, k, v, alpha, beta, bias=128.0):
+def step_error_bound(P0: quant.Packed, rows: quant.RowPlan, k, v, alpha, beta, bias=0.0):
     """Per-entry bound on |X_float32 - X| for X = D S + beta k (v^T - k^T D S).
 
     Whatever the summation order, a float32 evaluation that adds n terms errs by at most
     gamma_n = n u / (1 - n u) times the sum of the terms' magnitudes (u = 2^-24).  The sum
     counted here covers every term the library adds: alpha_i S_ij, and beta k_i times
-    |v_j| + sum_m |alpha_m k_m| (|S_mj| + bias r_m c_j), the codes of code rows being stored
-    with an offset of at most `bias` levels.  n is d_k plus a margin for the few products
-    and sums around the column reduction.
+    |v_j| + sum_m |alpha_m k_m| (|S_mj| + bias r_m c_j).  The library sums signed codes
+    (bias 0); an evaluation that summed codes stored with an offset of `bias` levels would
+    carry the extra term.  n is d_k plus a margin for the few products and sums around the
+    column reduction.
     """
     S = quant.dequantize(P0, rows)
     N, dk, dv = S.shape

@@ -154,6 +154,96 @@ def test_step_teacher_forced(torch, name, wl, nL, B, T):
     rig.close()
 
 
+def _degenerate_states(rig, seed):
+    """Float states with the method's special cases, one per state index; the rest random."""
+    g = np.random.default_rng(seed)
+    dk, dv = rig.dk, rig.dv
+    X = g.standard_normal((rig.N, dk, dv))
+    X[0] = 0.0                                          # all zero: r = 1, c = 1, codes 0
+    X[1, 3, :] = 0.0                                    # a zero row ...
+    X[1, :, 5] = 0.0                                    # ... and a zero column
+    X[2] *= 1e-10                                       # row factors and column scales clamp at 2^-14
+    X[3] *= 1e9                                         # row factors near or at the binary16 maximum
+    X[4] = np.outer(g.standard_normal(dk), g.standard_normal(dv))   # rank one
+    X[5] = 0.0
+    X[5, 7, 9] = 3.0                                    # a single nonzero entry
+    X[6] = np.abs(X[6])                                 # one sign only
+    return X
+
+
+@pytest.mark.parametrize("wl", [configs.GDN_DECODE, configs.KDA_DECODE], ids=["gdn", "kda"])
+def test_degenerate_states_pack_and_step(torch, wl):
+    """Zero states, zero rows and columns, clamped scales, rank-one and single-entry states: pack, one step
+    with the workload's inputs, and one step with alpha = 1, beta = 0 (the update is the identity, so the
+    step requantizes the dequantized state)."""
+    import quantized_delta_rule_02_amd as sq
+    say(f"degenerate states {wl.name}")
+    B = 1
+    rig = _rig(wl, 1, B)
+    X = _degenerate_states(rig, 17)
+    X32 = X.astype(np.float32).astype(np.float64)
+    sq.sq_pack(rig.pool, 0, 1, B, rig.slots, rig._t(X32.reshape(-1), torch.float32))
+    torch.cuda.synchronize()
+    zeros = np.zeros((rig.N, rig.dv))
+    P = quant.quantize(X32, rig.rows, wl.grid)
+    R = compare_step(X32, zeros, rig.rows, wl.grid, zeros, rig.export_packed(), P)
+    assert R.ok(), R.failures
+    q, k, v, beta = rig.inputs(1)
+    alpha = rig.alpha_states()
+    rig.import_packed(P)
+    y_g = rig.step(q[0], k[0], v[0], beta[0])
+    P2, y, Xo = packed_step(P, rig.rows, q[0], k[0], v[0], alpha, beta[0], wl.grid)
+    R = compare_step(Xo, y, rig.rows, wl.grid, y_g, rig.export_packed(), P2,
+                     x_err=step_error_bound(P, rig.rows, k[0], v[0], alpha, beta[0]))
+    say(R)
+    assert R.ok(), R.failures
+    # identity update: alpha = 1, beta = 0
+    rig.import_packed(P)
+    ones = np.ones_like(alpha)
+    b0 = np.zeros_like(beta[0])
+    y_t = torch.zeros(rig.N * rig.dv, dtype=torch.float32, device="cuda")
+    sq.sq_state_step(rig.pool, 0, 1, B, rig.slots, rig._t(q[0].reshape(-1), torch.float32),
+                     rig._t(k[0].reshape(-1), torch.float32), rig._t(v[0].reshape(-1), torch.float32),
+                     rig._t(ones.reshape(-1), torch.float32), rig._t(b0, torch.float32), y_t)
+    torch.cuda.synchronize()
+    P3, y3, X3 = packed_step(P, rig.rows, q[0], k[0], v[0], ones, b0, wl.grid)
+    assert np.array_equal(X3, quant.dequantize(P, rig.rows))
+    R = compare_step(X3, y3, rig.rows, wl.grid, y_t.cpu().numpy().reshape(rig.N, rig.dv).astype(np.float64),
+                     rig.export_packed(), P3, x_err=step_error_bound(P, rig.rows, k[0], v[0], ones, b0))
+    say(R)
+    assert R.ok(), R.failures
+    rig.close()
+
+
+def test_empty_calls_touch_nothing(torch):
+    """batch = 0 or n_layers = 0 is a valid empty call: status OK, no byte of the pool or the outputs changes;
+    a layer range outside the plan is still an error."""
+    import quantized_delta_rule_02_amd as sq
+    say("empty calls")
+    B = 2
+    rig = _rig(configs.GDN_DECODE, 1, B)
+    rig.import_packed(_random_canonical(rig, 5))
+    torch.cuda.synchronize()
+    before = rig.mem.clone()
+    f0 = torch.empty(0, dtype=torch.float32, device="cuda")
+    i0 = torch.empty(0, dtype=torch.int32, device="cuda")
+    h0 = torch.empty(0, dtype=torch.int16, device="cuda")
+    y = torch.full((rig.N * rig.dv,), 7.0, dtype=torch.float32, device="cuda")
+    sq.sq_state_step(rig.pool, 0, 1, 0, i0, f0, f0, f0, f0, f0, y)
+    sq.sq_state_step(rig.pool, 0, 0, B, rig.slots, f0, f0, f0, f0, f0, y)
+    sq.sq_state_step(rig.pool, 1, 0, B, rig.slots, f0, f0, f0, f0, f0, y, flags=sq.SQ_STEP_SPLIT)
+    sq.sq_pack(rig.pool, 0, 0, B, rig.slots, f0)
+    sq.sq_unpack(rig.pool, 0, 0, B, rig.slots, f0)
+    sq.sq_export(rig.pool, 0, 1, 0, i0, h0, h0, h0)
+    sq.sq_import(rig.pool, 0, 0, B, rig.slots, h0, h0, h0)
+    with pytest.raises(sq.StepQError):
+        sq.sq_state_step(rig.pool, 2, 0, B, rig.slots, f0, f0, f0, f0, f0, y)
+    torch.cuda.synchronize()
+    assert torch.equal(rig.mem, before)
+    assert bool(torch.all(y == 7.0))
+    rig.close()
+
+
 ABSMAX = [("gdn", configs.GDN_DECODE, 1, 2, 3), ("kda", configs.KDA_DECODE, 1, 2, 3),
           ("outlier", configs.OUTLIER, 1, 1, 2)]
 

@@ -2,8 +2,9 @@
 
 The tie-aware comparison must accept the oracle's own result, reject planted
 mistakes, and its float32 error bound for the update must hold for a float32
-evaluation of the update done the way the library does it (codes stored with
-an offset, column sums of offset codes, the offset's sum taken off afterwards).
+evaluation of the update done the way the library does it (column sums of the
+signed codes), and for one that sums codes stored with an offset and takes the
+offset's sum off afterwards when the bound is told the offset.
 """
 import numpy as np
 
@@ -65,12 +66,13 @@ def test_error_bound_covers_float32_update():
     for seed, kda in [(0, True), (1, False), (2, True)]:
         rows, P, q, k, v, a, b = _case(seed, kda=kda)
         _, _, X = packed_step(P, rows, q, k, v, a, b, (1.0, 0.875, 0.75, 0.625))
-        X32 = _update_float32(P, rows, k, v, a, b, 128.0)
-        bound = step_error_bound(P, rows, k, v, a, b)
-        err = np.abs(X32 - X)
-        assert np.all(err <= bound)
-        # the bound is a bound, but not a vacuous one: well under the entries' own size
-        assert np.median(bound / np.maximum(np.abs(X), 1e-30)) < 1e-3
+        for off in (0.0, 128.0):
+            X32 = _update_float32(P, rows, k, v, a, b, off)
+            bound = step_error_bound(P, rows, k, v, a, b, bias=off)
+            err = np.abs(X32 - X)
+            assert np.all(err <= bound)
+            # the bound is a bound, but not a vacuous one: well under the entries' own size
+            assert np.median(bound / np.maximum(np.abs(X), 1e-30)) < 1e-3
 
 
 def test_compare_accepts_oracle_and_rejects_planted_mistakes():
