@@ -302,11 +302,21 @@ __device__ __forceinline__ uint32_t gather4(uint32_t r0, uint32_t r1, uint32_t r
     return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 
+// A v_and_b32 whose result the compiler cannot see through.  Given a masked dword, it would
+// otherwise rewrite each byte's conversion as a bit-field extract plus a conversion (v_bfe_u32 issues
+// at the slow VALU rate) instead of one v_cvt_f32_ubyteN (1% on the step).
+template <uint32_t M>
+__device__ __forceinline__ uint32_t and_opaque(uint32_t x) {
+    uint32_t r;
+    __asm__("v_and_b32 %0, %1, %2" : "=v"(r) : "i"(M), "v"(x));
+    return r;
+}
+
 // fast unpack of one lane's 16 stored (offset) codes to float (layout in internal.h)
 __device__ __forceinline__ void unpack4f(const uint32_t* d, float* o) {
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-        const uint32_t lo = d[w] & 0x0F0F0F0Fu, hi = (d[w] >> 4) & 0x0F0F0F0Fu;
+        const uint32_t lo = and_opaque<0x0F0F0F0Fu>(d[w]), hi = and_opaque<0x0F0F0F0Fu>(d[w] >> 4);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             o[8 * w + k] = (float)((lo >> (8 * k)) & 0xFFu);
@@ -317,7 +327,7 @@ __device__ __forceinline__ void unpack4f(const uint32_t* d, float* o) {
 __device__ __forceinline__ void unpack6f(const uint32_t* d, float* o) {
 #pragma unroll
     for (int w = 0; w < 3; ++w) {
-        const uint32_t x = d[w] & 0x3F3F3F3Fu;
+        const uint32_t x = and_opaque<0x3F3F3F3Fu>(d[w]);
 #pragma unroll
         for (int k = 0; k < 4; ++k) o[4 * w + k] = (float)((x >> (8 * k)) & 0xFFu);
     }
@@ -332,7 +342,7 @@ __device__ __forceinline__ void unpack6f(const uint32_t* d, float* o) {
 __device__ __forceinline__ void unpack2f(uint32_t lo, float* o) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t x = (lo >> (2 * k)) & 0x03030303u;
+        const uint32_t x = and_opaque<0x03030303u>(lo >> (2 * k));
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[4 * k + j] = (float)((x >> (8 * j)) & 0xFFu);
     }
@@ -342,7 +352,7 @@ __device__ __forceinline__ void unpack3f(uint32_t lo, uint32_t hi, float* o) {
     const uint32_t H = (hi & 0xFu) | ((hi << 4) & 0xF00u) | ((hi << 8) & 0xF0000u) | ((hi << 12) & 0xF000000u);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t x = ((lo >> (2 * k)) & 0x03030303u) | (((H >> k) & 0x01010101u) << 2);
+        const uint32_t x = and_opaque<0x03030303u>(lo >> (2 * k)) | (((H >> k) & 0x01010101u) << 2);
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[4 * k + j] = (float)((x >> (8 * j)) & 0xFFu);
     }
