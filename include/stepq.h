@@ -139,7 +139,8 @@ sq_status sq_calib_generate(uint64_t seed, int32_t layer, int32_t head, int32_t 
  * The caller owns the pool memory: n_slots slots of desc.slot_bytes each.  A
  * request's state for (layer l, head h) lives in its slot at the plan's
  * offset for (l, h).  Binding copies the plan's layout tables to the current
- * device (the pool object owns those small allocations until destroyed). */
+ * device (the pool object owns those small allocations until destroyed); calls
+ * on the pool must run with that device current, otherwise SQ_ERR_ARG. */
 sq_status sq_pool_bytes(const sq_plan* plan, int32_t n_slots, size_t* bytes);
 sq_status sq_pool_create(const sq_plan* plan, void* d_pool, size_t pool_bytes, int32_t n_slots,
                          sq_pool** out);

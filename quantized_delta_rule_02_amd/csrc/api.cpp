@@ -369,6 +369,13 @@ extern "C" sq_status sq_pool_create(const sq_plan* p, void* d_pool, size_t pool_
 
 static sq_status check_range(const sq_pool* pl, int32_t layer0, int32_t n_layers, int32_t batch) {
     if (!pl) { set_error("pool is NULL"); return SQ_ERR_ARG; }
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != pl->device) {
+        set_error("pool bound on device %d, current device %d", pl->device, dev);
+        return SQ_ERR_ARG;
+    }
     if (layer0 < 0 || n_layers < 0 || layer0 + n_layers > pl->L) {
         set_error("layers [%d, %d) outside the plan's %d layers", layer0, layer0 + n_layers, pl->L);
         return SQ_ERR_PLAN_MISMATCH;
