@@ -296,6 +296,43 @@ def test_split_arrangement_is_bitwise_fused(torch):
     rig.close()
 
 
+def test_split_arrangement_with_stream_delays(torch):
+    """The split arrangement's event ordering under delays: long matrix products queued on the second
+    stream (the fit + pack kernels start late) or on the main stream (the readout kernels start late,
+    the fit must wait for them) leave bytes and readout identical to the fused kernel."""
+    wl = configs.GDN_DECODE
+    say("split with stream delays gdn")
+    rig = _rig(wl, 1, 4)
+    P = quant.quantize(rig.warm_state(steps=64), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(2)
+    import quantized_delta_rule_02_amd as sq
+    aux = torch.cuda.Stream()
+    big = torch.randn(4096, 4096, device="cuda")
+    sink = torch.empty_like(big)
+
+    def busy(stream):
+        with torch.cuda.stream(stream):
+            for _ in range(4):
+                torch.mm(big, big, out=sink)
+
+    def run(flags, s_aux, delay_on):
+        rig.import_packed(P)
+        ys = []
+        for t in range(2):
+            if delay_on is not None:
+                busy(delay_on)
+            ys.append(rig.step(q[t], k[t], v[t], beta[t], flags=flags, stream_aux=s_aux))
+        return ys, rig.mem.clone()
+
+    ref_ys, ref_mem = run(0, None, None)
+    for delay_on in (aux, torch.cuda.current_stream()):
+        ys, mem = run(sq.SQ_STEP_SPLIT, aux, delay_on)
+        assert all(np.array_equal(a, b) for a, b in zip(ys, ref_ys))
+        assert torch.equal(mem, ref_mem)
+    torch.cuda.synchronize()
+    rig.close()
+
+
 def test_split_without_join_per_layer_equals_fused(torch):
     """Per-layer split calls that leave the fit running on the second stream (the caller joins once
     per step) give the same bytes and readout as one fused call over all layers."""
