@@ -26,6 +26,9 @@
  *     current device); "h_" or unprefixed pointers in sq_plan_cfg are host.
  *   - Streams are passed as void* and hold a hipStream_t (NULL = the null stream).
  *   - Per-step arrays are laid out [n_layers][batch][H][d] (row-major, fp32).
+ *     Device inputs must be finite (the kernels run with IEEE mode off and do
+ *     not screen NaN or infinity); a non-finite input leaves the touched states
+ *     unspecified, never memory outside them.
  *   - A call over an empty range (batch = 0 or n_layers = 0) validates its
  *     sizes and returns SQ_OK without touching any array (they may be NULL).
  *   - Every call validates its arguments on the host before enqueuing work and
