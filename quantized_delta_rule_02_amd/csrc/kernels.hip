@@ -31,7 +31,7 @@
 
 #ifndef STEP_WAVES_PER_EU
 #define STEP_WAVES_PER_EU 4   // waves per SIMD the register allocation targets (128 VGPRs; the 128x128
-                              // step fits without spills)
+                              // step spills two registers, on the path of 16-bit groups only)
 #endif
 
 namespace sq {
@@ -689,7 +689,7 @@ k_state(StepParams a) {
 
     float X[EPL];
 
-    // ---- phase 1: unpack (signed codes / pivot values), column accumulations k^T D S, q^T D S
+    // ---- phase 1: unpack (c_j Q_ij on code rows, binary16 values on pivot rows), column sums k^T D S, q^T D S
     if constexpr (MODE == kModePack) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
