@@ -67,6 +67,31 @@ def per_state_bytes(dk, dv, form, state_bytes):
     return 2 * state_bytes + 4 * (2 * dk + 2 * dv + 1) + gate
 
 
+def int8_group_order(dk, dv):
+    """Row-major index of each byte of one INT8 comparator state, in the library's group-interleaved order
+    (16 / cpl rows x cpl columns per lane and group, cpl = max(1, dv / 64))."""
+    import numpy as np
+    cpl = max(1, dv // 64)
+    lpr, gr = dv // cpl, 16 // cpl
+    return np.arange(dk * dv).reshape(dk // gr, gr, lpr, cpl).transpose(0, 2, 1, 3).reshape(-1)
+
+
+def int8_states(S, n, dk, dv, chunk=4096):
+    """Uniform INT8 per-row states of the float states S [n][dk][dv]: group-interleaved codes and row scales."""
+    import torch
+    order = torch.as_tensor(int8_group_order(dk, dv), device=S.device)
+    codes = torch.empty(n, dk * dv, dtype=torch.int8, device=S.device)
+    scales = torch.empty(n, dk, dtype=torch.float32, device=S.device)
+    Sv = S.view(n, dk, dv)
+    for i0 in range(0, n, chunk):
+        blk = Sv[i0:i0 + chunk]
+        sc = (blk.abs().amax(dim=2) / 127.0).clamp_min(1e-30)
+        scales[i0:i0 + chunk] = sc
+        q = torch.clamp(torch.round(blk / sc[:, :, None]), -127, 127).to(torch.int8)
+        codes[i0:i0 + chunk] = q.reshape(-1, dk * dv)[:, order]
+    return codes.reshape(-1), scales.reshape(-1)
+
+
 def time_calls(fn, n, warm=2):
     """Mean milliseconds per call over n calls on torch's current stream (HIP events)."""
     import torch
@@ -203,20 +228,13 @@ def outlier_comparison(sq, torch, dev, steps):
     pool.close()
     plan.close()
     del mem
-    codes8 = torch.empty(n * dk * dv, dtype=torch.int8, device=dev)
-    scales8 = torch.empty(n * dk, dtype=torch.float32, device=dev)
-    Sv, Cv, Rv = S.view(n, dk, dv), codes8.view(n, dk, dv), scales8.view(n, dk)
-    for i0 in range(0, n, 4096):
-        blk = Sv[i0:i0 + 4096]
-        sc = (blk.abs().amax(dim=2) / 127.0).clamp_min(1e-30)
-        Rv[i0:i0 + 4096] = sc
-        Cv[i0:i0 + 4096] = torch.clamp(torch.round(blk / sc[:, :, None]), -127, 127).to(torch.int8)
+    codes8, scales8 = int8_states(S, n, dk, dv)
     ms8 = time_calls(lambda: sq.sq_int8_step(sq.SQ_FORM_KDA, H, dk, dv, B, 0, L, B, ident, codes8, scales8, q, k, v,
                                              gate, beta, y), steps)
     by8 = per_state_bytes(dk, dv, 1, dk * dv + 4 * dk)
     out["int8_row"] = {"ms": ms8, "state_updates_per_s": n / (ms8 / 1e3), "GBps": n * by8 / (ms8 / 1e3) / 1e9,
                        "state_bytes": dk * dv + 4 * dk}
-    del codes8, scales8, Sv, Cv, Rv
+    del codes8, scales8
     ms32 = time_calls(lambda: sq.sq_fp32_step(sq.SQ_FORM_KDA, H, dk, dv, B, 0, L, B, ident, S, q, k, v, gate, beta,
                                               y), steps)
     by32 = per_state_bytes(dk, dv, 1, 4 * dk * dv)
@@ -301,20 +319,13 @@ def main():
         by32 = per_state_bytes(dk, dv, form, 4 * dk * dv)
         extras["fp32_step"] = {"ms": ms32, "state_updates_per_s": n_states / (ms32 / 1e3),
                                "GBps": n_states * by32 / (ms32 / 1e3) / 1e9, "state_bytes": 4 * dk * dv}
-        codes8 = torch.empty(n_states * dk * dv, dtype=torch.int8, device=dev)
-        scales8 = torch.empty(n_states * dk, dtype=torch.float32, device=dev)
-        Sv, Cv, Rv = S.view(n_states, dk, dv), codes8.view(n_states, dk, dv), scales8.view(n_states, dk)
-        for i0 in range(0, n_states, 8192):
-            blk = Sv[i0:i0 + 8192]
-            sc = (blk.abs().amax(dim=2) / 127.0).clamp_min(1e-30)
-            Rv[i0:i0 + 8192] = sc
-            Cv[i0:i0 + 8192] = torch.clamp(torch.round(blk / sc[:, :, None]), -127, 127).to(torch.int8)
+        codes8, scales8 = int8_states(S, n_states, dk, dv, chunk=8192)
         ms8 = time_calls(lambda: sq.sq_int8_step(form, H, dk, dv, B, 0, L, B, ident, codes8, scales8, q1, k1, v1,
                                                  gate, b1, y), args.steps)
         by8 = per_state_bytes(dk, dv, form, dk * dv + 4 * dk)
         extras["int8_step"] = {"ms": ms8, "state_updates_per_s": n_states / (ms8 / 1e3),
                                "GBps": n_states * by8 / (ms8 / 1e3) / 1e9, "state_bytes": dk * dv + 4 * dk}
-        del codes8, scales8, Sv, Cv, Rv
+        del codes8, scales8
     del S
     torch.cuda.empty_cache()
     aux = torch.cuda.Stream() if args.split else None

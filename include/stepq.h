@@ -204,13 +204,16 @@ sq_status sq_import(sq_pool* pool, int32_t layer0, int32_t n_layers, int32_t bat
 
 /* ---- comparators (same inputs, other state formats) --------------------
  * Uniform INT8 per-row state (the baseline the pages compare against): state
- * i = (layer * n_slots + slot) * H + head holds int8 codes [d_k][d_v] at
+ * i = (layer * n_slots + slot) * H + head holds d_k*d_v int8 codes at
  * d_codes + i*d_k*d_v and a binary32 row scale [d_k] at d_scales + i*d_k;
  * step: S = s_i Q, the same update and readout, s_i = max_j |X_ij| / 127,
- * Q = clamp(rint(X / s_i), +-127).  sq_fp32_step keeps float states d_S
- * [(layer * n_slots + slot) * H + head][d_k][d_v] (no quantization).
- * Alignment: d_codes to max(1, d_v / 64) bytes, d_S to 4 * max(1, d_v / 64)
- * bytes (one access per lane and row); otherwise SQ_ERR_ARG. */
+ * Q = clamp(rint(X / s_i), +-127).  The codes of a state are group-interleaved
+ * like the pool's 8-bit containers: with cpl = max(1, d_v / 64) columns per lane,
+ * lpr = d_v / cpl lanes and gr = 16 / cpl rows per group, code (i, j) sits at
+ * byte ((i / gr) * lpr + j / cpl) * 16 + (i % gr) * cpl + j % cpl of the state.
+ * sq_fp32_step keeps float states d_S [(layer * n_slots + slot) * H + head]
+ * [d_k][d_v] row-major (no quantization).  Alignment: d_codes to 16 bytes, d_S
+ * to 4 * cpl bytes; otherwise SQ_ERR_ARG. */
 sq_status sq_int8_step(int32_t form, int32_t n_heads, int32_t dim_k, int32_t dim_v, int32_t n_slots,
                        int32_t layer0, int32_t n_layers, int32_t batch, const int32_t* d_slots,
                        int8_t* d_codes, float* d_scales, const float* d_q, const float* d_k,

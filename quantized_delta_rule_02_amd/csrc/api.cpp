@@ -560,10 +560,10 @@ static sq_status cmp_step(bool int8, int32_t form, int32_t H, int32_t dk, int32_
         set_error("NULL device array");
         return SQ_ERR_ARG;
     }
-    // each lane reads its cpl adjacent entries of a row in one access
+    // INT8: one 16-byte access per lane and group; FP32: a lane's cpl adjacent entries of a row in one access
     const uintptr_t cpl = uintptr_t(cpl_of(dv));
-    if (int8 ? (reinterpret_cast<uintptr_t>(codes) % cpl != 0) : (reinterpret_cast<uintptr_t>(S) % (4 * cpl) != 0)) {
-        set_error("state array not aligned to %u bytes", unsigned(int8 ? cpl : 4 * cpl));
+    if (int8 ? (reinterpret_cast<uintptr_t>(codes) % 16 != 0) : (reinterpret_cast<uintptr_t>(S) % (4 * cpl) != 0)) {
+        set_error("state array not aligned to %u bytes", unsigned(int8 ? 16 : 4 * cpl));
         return SQ_ERR_ARG;
     }
     hipError_t e = launch_cmp(dk, dv, int8, form, H, n_slots, layer0, n_layers, batch, slots, codes, scales, S, q, k, v,

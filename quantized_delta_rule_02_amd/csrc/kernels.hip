@@ -1128,25 +1128,15 @@ struct CmpParams {
 };
 
 // Uniform INT8 per-row state and the unquantized FP32 state: same wave/lane
-// mapping as the packed step, row-major state storage.
+// mapping as the packed step.  The INT8 codes are stored group-interleaved like the
+// pool's 8-bit containers (16 bytes per lane per group of 16 / CPL rows), the FP32
+// state row-major.
 // A lane's CPL adjacent entries of one row (CPL = 1, 2 or 4; the offset of the first is a
 // multiple of CPL, so the access is naturally aligned).
-template <int CPL>
-__device__ __forceinline__ void cmp_load_i8(const int8_t* p, bool act, float* x) {
-    uint32_t v = 0;
-    if (act) {
-        if constexpr (CPL == 1) v = (uint8_t)*p;
-        else if constexpr (CPL == 2) v = *reinterpret_cast<const uint16_t*>(p);
-        else v = *reinterpret_cast<const uint32_t*>(p);
-    }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) x[c] = (float)(int8_t)(v >> (8 * c));
-}
-template <int CPL>
-__device__ __forceinline__ void cmp_store_i8(int8_t* p, uint32_t v) {
-    if constexpr (CPL == 1) *p = (int8_t)v;
-    else if constexpr (CPL == 2) *reinterpret_cast<uint16_t*>(p) = (uint16_t)v;
-    else *reinterpret_cast<uint32_t*>(p) = v;
+// Byte offset of (state st, group g, lane) in the group-interleaved INT8 state.
+template <class Sh>
+__device__ __forceinline__ size_t cmp_group_offset(size_t st, int g, int lane) {
+    return ((st * Sh::NG + (size_t)g) * Sh::LPR + (size_t)lane) * 16;
 }
 template <int CPL>
 __device__ __forceinline__ void cmp_load_f32(const float* p, bool act, float* x) {
@@ -1171,7 +1161,8 @@ __global__ void __launch_bounds__(nw_of(DK, DV) * 64)
 k_cmp(CmpParams a) {
     using Sh = Shape<DK, DV>;
     constexpr int CPL = Sh::CPL, LPR = Sh::LPR, RPW = Sh::RPW, NW = Sh::NW, EPL = Sh::EPL;
-    __shared__ float s_ck[DK], s_cq[DK], s_al[DK], s_bk[DK], s_sc[DK];
+    constexpr int GR = Sh::GR, GPW = Sh::GPW;
+    __shared__ float s_ck[DK], s_cq[DK], s_al[DK], s_bk[DK], s_sc[DK], s_so[DK];
     __shared__ float s_part[NW][2][DV];
     __shared__ float s_red[NW];
     const int sid = block_idx();
@@ -1186,11 +1177,11 @@ k_cmp(CmpParams a) {
     if (tid < DK) {
         const float kk = a.k[(size_t)sid * DK + tid], qq = a.q[(size_t)sid * DK + tid];
         const float al = (a.form == 1) ? a.gate[(size_t)sid * DK + tid] : a.gate[sid];
-        const float sc = INT8 ? a.scales[st * DK + tid] : 1.f;
-        s_ck[tid] = al * sc * kk;
-        s_cq[tid] = al * sc * qq;
-        s_al[tid] = al * sc;
+        s_ck[tid] = al * kk;
+        s_cq[tid] = al * qq;
+        s_al[tid] = al;
         s_bk[tid] = a.beta[sid] * kk;
+        if constexpr (INT8) s_so[tid] = a.scales[st * DK + tid];
         kq = kk * qq;
     }
 #pragma unroll
@@ -1201,12 +1192,28 @@ k_cmp(CmpParams a) {
     float U[CPL], P[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) U[c] = P[c] = 0.f;
+    if constexpr (INT8) {
+        // one 16-byte access per lane and group; codes + 128 -> float, then s_i Q_ij with one exact-offset FMA
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) {
+            uint32_t d[4] = {0u, 0u, 0u, 0u};
+            if (act) load_dw<4>(reinterpret_cast<const uint8_t*>(a.codes) + cmp_group_offset<Sh>(st, wave * GPW + g, lane), d);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] ^= 0x80808080u;
+            unpack8(d, &X[16 * g]);
+#pragma unroll
+            for (int r = 0; r < GR; ++r) {
+                const float so = s_so[wave * RPW + g * GR + r];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) X[16 * g + r * CPL + c] = fmaf(X[16 * g + r * CPL + c], so, -128.f * so);
+            }
+        }
+    }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
         const int t = wave * RPW + r;
-        // the lane's CPL adjacent entries of the row in one access
-        if constexpr (INT8) cmp_load_i8<CPL>(a.codes + (st * DK + t) * DV + col0, act, &X[r * CPL]);
-        else cmp_load_f32<CPL>(a.S + (st * DK + t) * DV + col0, act, &X[r * CPL]);
+        // FP32: the lane's CPL adjacent entries of the row in one access
+        if constexpr (!INT8) cmp_load_f32<CPL>(a.S + (st * DK + t) * DV + col0, act, &X[r * CPL]);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             U[c] = fmaf(s_ck[t], X[r * CPL + c], U[c]);
@@ -1270,17 +1277,23 @@ k_cmp(CmpParams a) {
             a.scales[st * DK + t] = s;
         }
         __syncthreads();
+        // Q = clamp(rint(X / s), +-127): magic-number rounding with the +128 offset, packed by bytes
+        constexpr float mb = kMagic + 128.f;
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const int t = wave * RPW + r;
-            const float inv = s_sc[t];
-            uint32_t packed = 0;
+        for (int g = 0; g < GPW; ++g) {
+            float m[16];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const float qv = med3(rintf(X[r * CPL + c] * inv), -127.f, 127.f);
-                packed |= ((uint32_t)(int)qv & 0xFFu) << (8 * c);
+            for (int r = 0; r < GR; ++r) {
+                const float inv = s_sc[wave * RPW + g * GR + r];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    m[r * CPL + c] = med3(fmaf(X[16 * g + r * CPL + c], inv, mb), mb - 127.f, mb + 127.f);
             }
-            if (act) cmp_store_i8<CPL>(a.codes + (st * DK + t) * DV + col0, packed);
+            uint32_t d[4];
+            pack8m(m, d);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] ^= 0x80808080u;
+            if (act) store_dw<4>(reinterpret_cast<uint8_t*>(a.codes) + cmp_group_offset<Sh>(st, wave * GPW + g, lane), d);
         }
     }
 }

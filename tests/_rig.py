@@ -19,6 +19,14 @@ from workloads.configs import GDN, UNIT_HEAD, Workload
 from _parity import from_canonical, to_canonical
 
 
+def int8_group_order(dk: int, dv: int) -> np.ndarray:
+    """Row-major index of each byte of one INT8 comparator state (the library stores the codes
+    group-interleaved: 16 / cpl rows x cpl columns per lane and group, cpl = max(1, dv / 64))."""
+    cpl = max(1, dv // 64)
+    lpr, gr = dv // cpl, 16 // cpl
+    return np.arange(dk * dv).reshape(dk // gr, gr, lpr, cpl).transpose(0, 2, 1, 3).reshape(-1)
+
+
 def oracle_unit_bits(wl: Workload, n_layers: int, calib_segments=2, calib_len=32):
     """Oracle planner on the first n_layers layers with a short calibration."""
     gates = gen.unit_gates(wl)[:n_layers]

@@ -137,7 +137,11 @@ def test_int8_comparator_full_outlier_pool(dev):
     S = torch.randn(n, dk, dv, device=dev, generator=tg) * 2
     m = S.abs().amax(dim=2, keepdim=True)
     scales = (m / 127).squeeze(2).contiguous()
-    codes = torch.clamp(torch.round(S / (m / 127)), -127, 127).to(torch.int8).contiguous()
+    codes_rm = torch.clamp(torch.round(S / (m / 127)), -127, 127).to(torch.int8).reshape(n, dk * dv)
+    from _rig import int8_group_order
+    order = torch.as_tensor(int8_group_order(dk, dv), device=dev)
+    codes = codes_rm[:, order].contiguous()         # the library's group-interleaved order
+    del codes_rm
     q = torch.randn(n, dk, device=dev, generator=tg)
     k = torch.randn(n, dk, device=dev, generator=tg)
     q = (q / q.norm(dim=1, keepdim=True)).contiguous()
@@ -147,7 +151,12 @@ def test_int8_comparator_full_outlier_pool(dev):
     gate = torch.tensor(gen.unit_gates(wl)[0], device=dev)[None].expand(B, H, dk).contiguous()
     slots = torch.arange(B, dtype=torch.int32, device=dev)
     pick = [0, 517, B - 1]
-    before = {b: (codes[b * H:(b + 1) * H].cpu().numpy().astype(np.int64),
+    def rowmajor(c):
+        out = torch.empty_like(c)
+        out[:, order] = c
+        return out.reshape(-1, dk, dv)
+
+    before = {b: (rowmajor(codes[b * H:(b + 1) * H]).cpu().numpy().astype(np.int64),
                   scales[b * H:(b + 1) * H].cpu().numpy().astype(np.float64)) for b in pick}
     y = torch.zeros(n, dv, device=dev)
     sq.sq_int8_step(1, H, dk, dv, B, 0, 1, B, slots, codes, scales, q, k, v, gate, beta, y)
@@ -163,6 +172,6 @@ def test_int8_comparator_full_outlier_pool(dev):
         assert np.allclose(sg, s1, rtol=1e-5)
         z = X / sg[:, :, None]
         Qz = np.clip(np.rint(z), -127, 127)
-        dq = codes[sl].cpu().numpy().astype(np.int64) - Qz
+        dq = rowmajor(codes[sl]).cpu().numpy().astype(np.int64) - Qz
         near = np.abs(np.abs(z - np.floor(z)) - 0.5) < 1e-3
         assert np.all(np.abs(dq) <= 1) and np.all((dq == 0) | near)

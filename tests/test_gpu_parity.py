@@ -470,7 +470,10 @@ def test_int8_and_fp32_comparators(torch, wl):
         codes[slots[b] * H:(slots[b] + 1) * H] = Q0[b * H:(b + 1) * H]
         scales[slots[b] * H:(slots[b] + 1) * H] = s0[b * H:(b + 1) * H]
         Sfull[slots[b] * H:(slots[b] + 1) * H] = S[b * H:(b + 1) * H]
-    dc, ds, dS = t(codes, torch.int8), t(scales), t(Sfull)
+    from _rig import int8_group_order
+    order = int8_group_order(dk, dv)
+    dc = t(codes.reshape(n_slots * H, dk * dv)[:, order], torch.int8)
+    ds, dS = t(scales), t(Sfull)
     y8 = torch.zeros(N * dv, device="cuda")
     y32 = torch.zeros(N * dv, device="cuda")
     form = 0 if wl.form == "gdn" else 1
@@ -481,7 +484,9 @@ def test_int8_and_fp32_comparators(torch, wl):
     torch.cuda.synchronize()
     Q1, s1, y_ref8, X8 = int8_step(Q0, s0, q, k, v, alpha, beta)
     X32, y_ref32 = delta_update(S.astype(np.float64), q, k, v, alpha, beta)
-    got_c = dc.cpu().numpy().reshape(n_slots * H, dk, dv)
+    got_c = np.empty((n_slots * H, dk * dv), np.int8)
+    got_c[:, order] = dc.cpu().numpy().reshape(n_slots * H, dk * dv)
+    got_c = got_c.reshape(n_slots * H, dk, dv)
     got_s = ds.cpu().numpy().reshape(n_slots * H, dk)
     got_S = dS.cpu().numpy().reshape(n_slots * H, dk, dv)
     rows_c = np.concatenate([got_c[slots[b] * H:(slots[b] + 1) * H] for b in range(B)]).astype(np.int64)

@@ -170,11 +170,14 @@ def test_argument_validation_status_codes():
     assert lib.sq_copy(None, None, 16, None) == -1
     assert lib.sq_int8_step(0, 32, 96, 128, 4, 0, 1, 1, None, None, None, None, None, None, None, None, None,
                             None) == -3
-    # comparator state arrays must allow one access per lane and row (never dereferenced here)
+    # comparator state arrays: INT8 codes 16-byte aligned (one access per lane and group), FP32 states
+    # aligned for one access per lane and row (never dereferenced here)
     fake = ctypes.c_void_p(0x10000)
     odd = ctypes.c_void_p(0x10001)
     assert lib.sq_int8_step(0, 32, 128, 128, 4, 0, 1, 1, fake, odd, fake, fake, fake, fake, fake, fake, fake,
                             None) == -1
+    assert lib.sq_int8_step(0, 32, 128, 128, 4, 0, 1, 1, fake, ctypes.c_void_p(0x10008), fake, fake, fake, fake,
+                            fake, fake, fake, None) == -1
     assert lib.sq_fp32_step(0, 32, 128, 128, 4, 0, 1, 1, fake, ctypes.c_void_p(0x10004), fake, fake, fake, fake,
                             fake, fake, None) == -1
     assert lib.sq_plan_create(None, ctypes.byref(ctypes.c_void_p())) == -1
