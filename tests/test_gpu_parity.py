@@ -373,6 +373,53 @@ def test_split_without_join_per_layer_equals_fused(torch):
     rig.close()
 
 
+def test_fused_step_replays_in_a_hip_graph(torch):
+    """The fused step captured once in a HIP graph and replayed: every replay, with eager work and
+    synchronizations between replays, equals the eager step on the same inputs (bytes and readout)."""
+    import quantized_delta_rule_02_amd as sq
+    wl = configs.GDN_DECODE
+    say("hip graph replay gdn")
+    rig = _rig(wl, 1, 4)
+    P = quant.quantize(rig.warm_state(steps=64), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(1)
+    t = lambda a: rig._t(np.ascontiguousarray(a).reshape(-1), torch.float32)
+    qs, ks, vs, bs, gate = t(q[0]), t(k[0]), t(v[0]), t(beta[0]), rig.gate_step()
+    y = torch.zeros(rig.N * rig.dv, dtype=torch.float32, device="cuda")
+
+    def step():
+        sq.sq_state_step(rig.pool, 0, 1, rig.B, rig.slots, qs, ks, vs, gate, bs, y)
+
+    n_rep = 4
+    rig.import_packed(P)
+    eager = []
+    for _ in range(n_rep):
+        step()
+        torch.cuda.synchronize()
+        eager.append((y.clone(), rig.mem.clone()))
+    rig.import_packed(P)
+    torch.cuda.synchronize()
+    before = rig.mem.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(rig.mem, before)    # capturing ran nothing
+    rig.import_packed(P)
+    torch.cuda.synchronize()
+    for i in range(n_rep):
+        y.fill_(-1.0)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager[i][0]), f"replay {i}: readout differs"
+        assert torch.equal(rig.mem, eager[i][1]), f"replay {i}: pool bytes differ"
+    del g
+    rig.close()
+
+
 def test_repeated_runs_are_deterministic(torch):
     wl = configs.KDA_DECODE
     say("determinism kda")
