@@ -143,7 +143,9 @@ sq_status sq_calib_generate(uint64_t seed, int32_t layer, int32_t head, int32_t 
  * request's state for (layer l, head h) lives in its slot at the plan's
  * offset for (l, h).  Binding copies the plan's layout tables to the current
  * device (the pool object owns those small allocations until destroyed); calls
- * on the pool must run with that device current, otherwise SQ_ERR_ARG. */
+ * on the pool must run with that device current, otherwise SQ_ERR_ARG.  A slot
+ * whose bytes are all zero holds the zero state (its scales are 0), so a new
+ * request's slot may be cleared instead of imported. */
 sq_status sq_pool_bytes(const sq_plan* plan, int32_t n_slots, size_t* bytes);
 sq_status sq_pool_create(const sq_plan* plan, void* d_pool, size_t pool_bytes, int32_t n_slots,
                          sq_pool** out);

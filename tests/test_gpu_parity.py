@@ -215,6 +215,25 @@ def test_degenerate_states_pack_and_step(torch, wl):
     rig.close()
 
 
+@pytest.mark.parametrize("wl", [configs.GDN_DECODE, configs.KDA_DECODE], ids=["gdn", "kda"])
+def test_zero_filled_slot_is_the_zero_state(torch, wl):
+    """A slot whose bytes are all zero (scales 0, offset codes 0) decodes to the zero state, so a fresh
+    request's slot can be cleared instead of imported: its first step equals the oracle's step from zero."""
+    say(f"zero-filled slots {wl.name}")
+    B = 2
+    rig = _rig(wl, 1, B, n_slots=4, slots=np.array([2, 0], np.int32))   # the pool memory starts zeroed
+    P0 = quant.quantize(np.zeros((rig.N, rig.dk, rig.dv)), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(1)
+    alpha = rig.alpha_states()
+    y_g = rig.step(q[0], k[0], v[0], beta[0])
+    P1, y, X = packed_step(P0, rig.rows, q[0], k[0], v[0], alpha, beta[0], wl.grid)
+    R = compare_step(X, y, rig.rows, wl.grid, y_g, rig.export_packed(), P1,
+                     x_err=step_error_bound(P0, rig.rows, k[0], v[0], alpha, beta[0]))
+    say(R)
+    assert R.ok(), R.failures
+    rig.close()
+
+
 def test_empty_calls_touch_nothing(torch):
     """batch = 0 or n_layers = 0 is a valid empty call: status OK, no byte of the pool or the outputs changes;
     a layer range outside the plan is still an error."""
