@@ -1298,10 +1298,26 @@ k_cmp(CmpParams a) {
     }
 }
 
+// Streaming copy for the achievable-bandwidth reference: each workgroup copies kCopyUnroll x 256
+// consecutive 16-byte vectors once, all loads before the stores, non-temporal both ways (5.85 TB/s
+// on 4 GiB against 4.75 for a grid-stride loop of single 16-byte copies).
 constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __global__ void __launch_bounds__(kCopyThreads)
-k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n, size_t stride) {
-    for (size_t i = (size_t)block_idx() * kCopyThreads + thread_idx(); i < n; i += stride) dst[i] = src[i];
+k_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
+    const size_t base = (size_t)block_idx() * (kCopyUnroll * kCopyThreads) + thread_idx();
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const size_t i = base + (size_t)u * kCopyThreads;
+        if (i < n) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const size_t i = base + (size_t)u * kCopyThreads;
+        if (i < n) __builtin_nontemporal_store(v[u], dst + i);
+    }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1397,10 +1413,10 @@ hipError_t launch_cmp(int dk, int dv, bool int8, int form, int n_heads, int n_sl
 hipError_t launch_copy(const void* src, void* dst, size_t n_bytes, hipStream_t s) {
     const size_t n = n_bytes / 16;
     if (n == 0) return hipSuccess;
-    size_t blocks = (n + kCopyThreads - 1) / kCopyThreads;
-    if (blocks > 256 * 32) blocks = 256 * 32;
-    k_copy<<<dim3((unsigned)blocks), dim3(kCopyThreads), 0, s>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst), n,
-                                                                 blocks * kCopyThreads);
+    const size_t per = size_t(kCopyUnroll) * kCopyThreads;
+    const size_t blocks = (n + per - 1) / per;
+    if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
+    k_copy<<<dim3((unsigned)blocks), dim3(kCopyThreads), 0, s>>>(static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
     return hipGetLastError();
 }
 

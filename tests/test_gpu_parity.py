@@ -579,6 +579,12 @@ def test_copy_kernel(torch):
     sq.sq_copy(a, b)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+    # a ragged length (not a whole number of a workgroup's 16 KiB chunks) stops at its last byte
+    c = torch.zeros_like(a)
+    n = 16 * 1001
+    sq.sq_copy(a, c, n_bytes=n)
+    torch.cuda.synchronize()
+    assert torch.equal(c[:n // 4], a[:n // 4]) and not bool(torch.any(c[n // 4:] != 0))
 
 
 def test_validate_mode_rejects_bad_slots(torch):
