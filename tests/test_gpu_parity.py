@@ -472,7 +472,7 @@ def _oracle_fp32_rounded(P0, rows, q, k, v, alpha, beta, grid):
 
 
 @pytest.mark.parametrize("name,wl,nL,B,T", [("tiny", configs.TINY, 1, 1, 64), ("gdn", configs.GDN_DECODE, 1, 1, 256),
-                                            ("kda", configs.KDA_DECODE, 1, 1, 64)],
+                                            ("kda", configs.KDA_DECODE, 1, 1, 256)],
                          ids=["tiny", "gdn", "kda"])
 def test_free_running_drift(torch, name, wl, nL, B, T):
     """Free-running steps from the same packed start.
