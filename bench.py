@@ -388,7 +388,22 @@ def main():
         aux2 = torch.cuda.Stream()
         mss = time_calls(lambda: sq.sq_state_step(pool, 0, L, B, slots, q1, k1, v1, gate, b1, y, stream_aux=aux2,
                                                   flags=sq.SQ_STEP_SPLIT), args.steps)
-        extras["split2"] = {"ms": mss, "state_updates_per_s": per_step / (mss / 1e3)}
+        # time to y: the main stream's part of a split call (the readout kernels), the fit + pack of the call
+        # left running on the second stream; the next call starts after it, so calls never overlap
+        cur = torch.cuda.current_stream()
+        t_y = 0.0
+        for i in range(args.warmup + args.steps):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(cur)
+            sq.sq_state_step(pool, 0, L, B, slots, q1, k1, v1, gate, b1, y, stream_aux=aux2,
+                             flags=sq.SQ_STEP_SPLIT | sq.SQ_STEP_NO_JOIN)
+            a1.record(cur)
+            cur.wait_stream(aux2)
+            torch.cuda.synchronize()
+            if i >= args.warmup:
+                t_y += a0.elapsed_time(a1)
+        extras["split2"] = {"ms": mss, "state_updates_per_s": per_step / (mss / 1e3),
+                            "time_to_y_ms": t_y / args.steps}
         # candidate-grid sweep on the same packed pool (the grid does not change the layout)
         units = sq.sq_plan_units(plan)["unit_bits"]
         sweep = {}
