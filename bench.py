@@ -25,7 +25,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# fp32 vector peak of the MI355X: 256 CUs x 2.4 GHz x 256 flops per CU and clock (128 FMA lanes)
+ALU_PEAK_TFLOPS = 256 * 2.4e9 * 256 / 1e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_state_step_serving6.txt")
+VALU_FILE = os.path.join(ROOT, "profiles", "pmc_state_step_serving6_valu.txt")
+PROFILED_WORKLOAD = "serving-36l-32h-256req-6bit"     # the workload the counter summaries were taken on
 KERNEL_SRC = os.path.join(ROOT, "quantized_delta_rule_02_amd", "csrc", "kernels.hip")
 
 
@@ -107,12 +111,12 @@ def time_calls(fn, n, warm=2):
     return e0.elapsed_time(e1) / n
 
 
-def traffic_per_launch():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def _profile_value(path, key):
+    """A figure from a committed rocprofv3 summary, if the summary matches this kernel source."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -120,9 +124,21 @@ def traffic_per_launch():
     if kv.get("kernel_source_sha256") != sha:
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
+
+
+def traffic_per_launch():
+    """HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, calibrated on the copy kernel)."""
+    return _profile_value(TRAFFIC_FILE, "hbm_bytes_per_launch")
+
+
+def algorithmic_flops(n_states, dk, dv, n_grid):
+    """Arithmetic the step must do per call: (12 + 5 G) d_k d_v flops per state update -- the two column
+    sums (4), the rank-one update (2), dequantization (1), and the requantization with G candidates
+    (5 + 5 G)."""
+    return n_states * (12 + 5 * n_grid) * dk * dv
 
 
 def _oracle_sample(wl, seed, n=64):
@@ -353,7 +369,12 @@ def main():
 
     alg = algorithmic_bytes(plan, B, sq)
     achieved = alg / (ms / 1e3) / 1e9
-    traffic = traffic_per_launch()
+    flops = algorithmic_flops(per_step, dk, dv, len(wl.grid))
+    tflops = flops / (ms / 1e3) / 1e12
+    profiled = wl.name == PROFILED_WORKLOAD
+    traffic = traffic_per_launch() if profiled else None
+    valu_per_wave = _profile_value(VALU_FILE, "valu_per_wave") if profiled else None
+    waves = per_step * 4                                  # four wave64 per 128x128 state
     desc = plan.desc
     out = {
         "metric": "state-updates/s (req·head·step) + achieved HBM GB/s, 6-bit packed state",
@@ -375,11 +396,18 @@ def main():
                    "state_updates_per_step": per_step,
                    "compression_vs_fp32": round(desc["compression_vs_fp32"], 4),
                    "stored_bits_per_entry": round(desc["stored_bits_per_entry"], 4)},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
+        # the step is bound by VALU issue (the exact column fit), not by HBM
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / ALU_PEAK_TFLOPS,
                      "traffic": None if traffic is None else traffic,
-                     "algorithmic_bytes_per_launch": alg, "kernel": "k_state<128,128,step>",
-                     "launch_ms": ms},
+                     "algorithmic_flops_per_launch": flops, "kernel": "k_state<128,128,step>",
+                     "launch_ms": ms,
+                     "hbm": {"achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": achieved / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": alg},
+                     "valu_issue": None if valu_per_wave is None else {
+                         "instructions_per_launch": valu_per_wave * waves,
+                         "wave_instructions_per_cu_per_clock": valu_per_wave * waves / (ms / 1e3) / (256 * 2.4e9),
+                         "peak": 2.0}},
         "wall_s_timed": wall,
     }
     if not args.no_extras:
