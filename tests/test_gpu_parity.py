@@ -439,6 +439,34 @@ def test_fused_step_replays_in_a_hip_graph(torch):
     rig.close()
 
 
+def test_saved_plan_drives_an_identical_pool(torch):
+    """A plan saved to bytes and loaded back binds a pool whose step gives the same bytes and readout
+    (the plan as an offline artefact: computed once, reused by every serving process)."""
+    import quantized_delta_rule_02_amd as sq
+    wl = configs.KDA_DECODE
+    say("saved plan kda")
+    rig = _rig(wl, 1, 2)
+    P = quant.quantize(rig.warm_state(steps=32), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(1)
+    rig.import_packed(P)
+    y_a = rig.step(q[0], k[0], v[0], beta[0])
+    mem_a = rig.mem.clone()
+    plan_b = sq.sq_plan_load(sq.sq_plan_save(rig.plan))
+    assert plan_b.desc == rig.plan.desc
+    mem_b = torch.zeros_like(rig.mem)
+    pool_b = sq.sq_pool_create(plan_b, mem_b, rig.n_slots)
+    rig.pool, pool_a = pool_b, rig.pool          # drive the rig through the loaded plan's pool
+    rig.mem, mem_keep = mem_b, rig.mem
+    rig.import_packed(P)
+    y_b = rig.step(q[0], k[0], v[0], beta[0])
+    assert np.array_equal(y_a, y_b)
+    assert torch.equal(mem_b, mem_a)
+    rig.pool, rig.mem = pool_a, mem_keep
+    pool_b.close()
+    plan_b.close()
+    rig.close()
+
+
 def test_repeated_runs_are_deterministic(torch):
     wl = configs.KDA_DECODE
     say("determinism kda")
