@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the comparators (INT8 per-row, FP32), the split arrangement, the candidate-grid "
-                         "sweep, the 4-bit budgets, the copy reference and the dual-axis outlier pool")
+                         "sweep, the 4-bit budgets, the copy reference, the dual-axis outlier pool and the "
+                         "cache-resident decode pools")
     return ap.parse_args()
 
 
@@ -192,6 +193,68 @@ def cpu_baseline(wl, seconds):
             "sample": f"{done} state updates over {cores} processes (each 64 sampled (layer, head) states of the "
                       f"workload with 6-bit rows, steps repeated for {2 * seconds / 3:.0f} s) plus {n1} in one "
                       f"thread, by the float64 NumPy oracle, BLAS limited to one thread per process"}
+
+
+def small_pools(sq, torch, dev, n_steps=256, per_graph=32):
+    """The decode workloads whose pools fit in the 256 MB last-level cache (GDN: 64 requests x 32 heads;
+    KDA: 128 requests x 32 heads; 128x128 states, 6.0-bit budget): a step is a few microseconds of work,
+    so launches matter.  Time per step over n_steps steps launched one by one, and replayed from a HIP
+    graph holding per_graph steps (the graph is replayed n_steps / per_graph times)."""
+    import numpy as np
+    from workloads import configs, gen
+    out = {}
+    for wl in (configs.GDN_DECODE, configs.KDA_DECODE):
+        L, H, dk, dv, B = wl.n_layers, wl.n_heads, wl.d_k, wl.d_v, wl.batch
+        n = L * B * H
+        form = sq.SQ_FORM_GDN if wl.form == "gdn" else sq.SQ_FORM_KDA
+        unit = sq.SQ_UNIT_HEAD if wl.unit == "head" else sq.SQ_UNIT_ROW
+        plan = sq.sq_plan_create(form=form, unit=unit, n_layers=L, n_heads=H, d_k=dk, d_v=dv, widths=wl.widths,
+                                 budget_milli=wl.budget_milli, pivot_ppm=wl.pivot_ppm, grid=wl.grid,
+                                 gate=gen.unit_gates(wl), impact=gen.impact_scores(wl),
+                                 calib_seed=gen.calib_seed(wl), calib_segments=wl.calib_segments,
+                                 calib_len=wl.calib_len)
+        mem = torch.zeros(sq.sq_pool_bytes(plan, wl.n_slots), dtype=torch.uint8, device=dev)
+        pool = sq.sq_pool_create(plan, mem, wl.n_slots)
+        slots = torch.tensor(gen.slot_map(wl), dtype=torch.int32, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(43)
+        sq.sq_pack(pool, 0, L, B, slots, torch.randn(n * dk * dv, device=dev, generator=g))
+        q = torch.randn(n, dk, device=dev, generator=g)
+        k = torch.randn(n, dk, device=dev, generator=g)
+        q = (q / q.norm(dim=1, keepdim=True)).reshape(-1).contiguous()
+        k = (k / k.norm(dim=1, keepdim=True)).reshape(-1).contiguous()
+        v = torch.randn(n * dv, device=dev, generator=g)
+        beta = torch.sigmoid(torch.randn(n, device=dev, generator=g))
+        gt = torch.tensor(gen.unit_gates(wl), device=dev)
+        gate = (gt[:, None, :].expand(L, B, H) if form == sq.SQ_FORM_GDN
+                else gt[:, None].expand(L, B, H, dk)).contiguous().reshape(-1)
+        y = torch.empty(n * dv, device=dev)
+
+        def step():
+            sq.sq_state_step(pool, 0, L, B, slots, q, k, v, gate, beta, y)
+
+        eager_ms = time_calls(step, n_steps)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(per_graph):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        reps = max(1, n_steps // per_graph)
+        graph_ms = time_calls(graph.replay, reps) / per_graph
+        alg = algorithmic_bytes(plan, B, sq)
+        out[wl.name] = {"states_per_step": n, "eager_us_per_step": eager_ms * 1e3,
+                        "graph_us_per_step": graph_ms * 1e3,
+                        "state_updates_per_s_graph": n / (graph_ms / 1e3),
+                        "effective_GBps_graph": alg / (graph_ms / 1e3) / 1e9,
+                        "pool_MB": round(sq.sq_pool_bytes(plan, wl.n_slots) / 1e6, 1)}
+        del graph
+        pool.close()
+        plan.close()
+        del mem
+    torch.cuda.empty_cache()
+    return out
 
 
 def outlier_comparison(sq, torch, dev, steps):
@@ -506,6 +569,7 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
         extras["outlier_dual_axis"] = outlier_comparison(sq, torch, dev, args.steps)
+        extras["small_pools"] = small_pools(sq, torch, dev)
         out["extras"] = extras
     if cpu is not None:
         out["cpu_baseline"] = cpu
