@@ -283,7 +283,8 @@ template <int DK, int DV>
 struct StepSmem {
     float4 acc[DK];    // column accumulation: A k, A q (code rows), alpha k, alpha q (pivot rows)
     float4 upd[DK];    // update: A = alpha r_old (code rows), beta k, alpha (pivot rows), unused
-    float4 fit[DK];    // requantization: 1 / r_new, sqrt(w) r_new, 1 / qmax, qmax
+    float4 fit[DK];    // requantization: 1 / r_new, sqrt(w) r_new, -sqrt(w) r_new / 2, 1/2 - qmax
+    float iq[DK];      // 1 / qmax (0 on pivot rows)
     float2 fin[DK];    // final rounding bounds: magic + container bias -/+ qmax
     float rn[DK];      // new binary16 row factor
     float w[DK];
@@ -520,12 +521,25 @@ __device__ __forceinline__ void round_pack_uniform(const float* X, const float* 
 // impact-weighted error F = c^2 sum_i (sqrt(w_i) r_i)^2 (t_ij / c - Q_ij)^2 of the
 // wave's rows, combined over the waves; the best candidate so far is kept (strict <).
 // part[] is read by every wave after the barrier: a later round must synchronize first.
+//
+// The residual y - Q of y = |t| / c >= 0 and Q = min(rint(y), qmax) comes without forming Q:
+// with a = y + 1/2 - qmax (one FMA; qmax is an integer, so fract(a) = fract(y + 1/2)),
+//   y <= qmax + 1/2:  a <= 1 and fract(a) - 1/2 = y - round(y), and fract(a) >= a;
+//   y >  qmax + 1/2:  a > 1, the code clips to qmax and the residual is y - qmax = a - 1/2 > fract(a) - 1/2;
+// so y - Q = max(a, fract(a)) - 1/2 in both cases (at an exact half-way point either rounding leaves
+// the same squared residual).  Per candidate and entry: FMA, fract, max, the weight FMA and the
+// accumulating FMA.  a carries the rounding of a sum of magnitude up to qmax, about 2^-24 qmax,
+// the order of the float32 error that t itself already has.
 template <class Sh, int KG, bool FREE0, class Smem>
 __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float* c0, const float* grid, int g0,
                                            int n_grid, int wave, int lane, bool act, float* cbest, float* fbest) {
     constexpr int CPL = Sh::CPL, RPW = Sh::RPW, NW = Sh::NW;
     const int col0 = lane * CPL;
     float cg[KG][CPL], icg[KG][CPL], Fp[KG][CPL];
+    // the rows' LDS addresses are formed inside each round: hoisted out of the caller's round loop
+    // they would hold RPW registers across it
+    int rbase = wave * RPW;
+    if constexpr (!FREE0) __asm__ volatile("" : "+s"(rbase));
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
         const float gam = grid[min(g0 + j, n_grid - 1)];   // a short last round repeats a candidate
@@ -546,29 +560,30 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) __asm__ volatile("" : "+v"(icg[j][c]));
         }
-        const float4 f = sm.fit[wave * RPW + r];
-        const float qm = f.w, sw = f.y;
+        const float4 f = sm.fit[rbase + r];
+        const float sw = f.y, nsw = f.z, hq = f.w;
         // The error is odd in t and round-half-even is symmetric, so the fit works on |t| (a free
-        // source modifier) and the clamp is one v_min.  The row's KG x CPL chains advance in stages
-        // separated by empty asm statements: left alone, the scheduler runs each chain to its end
-        // before the next, and a wave then stalls on every dependent step.
-        float t[CPL], R[KG][CPL], E[KG][CPL];
+        // source modifier).  The first candidate of a round that starts at gamma = 1 cannot clip and
+        // skips the max.  The row's KG x CPL chains advance in stages separated by empty asm
+        // statements: left alone, the scheduler runs each chain to its end before the next, and a
+        // wave then stalls on every dependent step.
+        float t[CPL], A[KG][CPL], E[KG][CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) t[c] = fabsf(X[r * CPL + c]);
 #pragma unroll
         for (int j = 0; j < KG; ++j)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) R[j][c] = rintf(t[c] * icg[j][c]);
+            for (int c = 0; c < CPL; ++c) A[j][c] = fmaf(t[c], icg[j][c], hq);
 #pragma unroll
         for (int j = 0; j < KG; ++j)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) __asm__ volatile("" : "+v"(R[j][c]));
+            for (int c = 0; c < CPL; ++c) __asm__ volatile("" : "+v"(A[j][c]));
 #pragma unroll
         for (int j = 0; j < KG; ++j)
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const float Qc = (FREE0 && j == 0) ? R[j][c] : fminf(R[j][c], qm);
-                E[j][c] = sw * fmaf(t[c], icg[j][c], -Qc);
+                const float fr = __builtin_amdgcn_fractf(A[j][c]);
+                E[j][c] = (FREE0 && j == 0) ? fr : fmaxf(A[j][c], fr);
             }
 #pragma unroll
         for (int j = 0; j < KG; ++j)
@@ -577,7 +592,10 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
 #pragma unroll
         for (int j = 0; j < KG; ++j)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) Fp[j][c] = fmaf(E[j][c], E[j][c], Fp[j][c]);
+            for (int c = 0; c < CPL; ++c) {
+                const float ew = fmaf(E[j][c], sw, nsw);
+                Fp[j][c] = fmaf(ew, ew, Fp[j][c]);
+            }
     }
     if (act) {
 #pragma unroll
@@ -883,8 +901,9 @@ k_state(StepParams a) {
             if (!piv && m > 0.f)   // dual-axis sqrt(m / w); the ablation's per-row absmax m / qmax
                 rn = scale_fp16(a.quant_mode == 0 ? __builtin_sqrtf(m * __builtin_amdgcn_rcpf(w)) : m / qmax);
             sm.rn[t] = rn;
-            sm.fit[t] = make_float4(__builtin_amdgcn_rcpf(rn), piv ? 0.f : __builtin_sqrtf(w) * rn,
-                                    piv ? 0.f : __builtin_amdgcn_rcpf(qmax), qmax);
+            const float sw = piv ? 0.f : __builtin_sqrtf(w) * rn;
+            sm.fit[t] = make_float4(__builtin_amdgcn_rcpf(rn), sw, -0.5f * sw, 0.5f - qmax);
+            sm.iq[t] = piv ? 0.f : __builtin_amdgcn_rcpf(qmax);
             const float mb = kMagic + (float)bias_of(gbits[t / GR]);
             sm.fin[t] = make_float2(mb - qmax, mb + qmax);
         }
@@ -908,7 +927,7 @@ k_state(StepParams a) {
             const int t0 = wave * RPW + g * GR;
             // rows are sorted by width, so a group whose first and last rows agree has one qmax
             if (sm.rb[t0] == sm.rb[t0 + GR - 1]) {
-                const float iq = sm.fit[t0].z;
+                const float iq = sm.iq[t0];
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     float mg = 0.f;
@@ -919,7 +938,7 @@ k_state(StepParams a) {
             } else {
 #pragma unroll
                 for (int r = 0; r < GR; ++r) {
-                    const float iq = sm.fit[t0 + r].z;
+                    const float iq = sm.iq[t0 + r];
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) c0p[c] = fmaxf(c0p[c], fabsf(X[16 * g + r * CPL + c]) * iq);
                 }
