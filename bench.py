@@ -324,6 +324,31 @@ def outlier_comparison(sq, torch, dev, steps):
     return out
 
 
+def valu_ceiling(sq, torch, dev):
+    """FMA issue rate of the library's probe (independent chains, vector-register operands) with residency
+    capped at 4 waves per SIMD (the step's: 128 VGPRs) and at 8, in wave-instructions per CU per clock at
+    the nominal 2.4 GHz, the unit of the step's own rate beside it."""
+    res = {}
+    buf = torch.empty(65536 * 256, dtype=torch.float32, device=dev)     # 65,536 workgroups of 4 waves
+    for w in (4, 8):
+        try:
+            sq.sq_valu_probe(w, buf)
+        except sq.StepQError as e:
+            res[f"waves_per_simd_{w}"] = {"error": str(e)}
+            continue
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            n_fma, fit = sq.sq_valu_probe(w, buf)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 3
+        res[f"waves_per_simd_{w}"] = {"fma_per_cu_per_clock": n_fma / (t / 1e3) / (256 * 2.4e9),
+                                      "resident_workgroups_per_cu": fit, "ms": t}
+    del buf
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -467,10 +492,12 @@ def main():
                      "launch_ms": ms,
                      "hbm": {"achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                              "frac": achieved / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": alg},
-                     "valu_issue": None if valu_per_wave is None else {
-                         "instructions_per_launch": valu_per_wave * waves,
-                         "wave_instructions_per_cu_per_clock": valu_per_wave * waves / (ms / 1e3) / (256 * 2.4e9),
-                         "peak": 2.0}},
+                     "valu_issue": {
+                         "instructions_per_launch": None if valu_per_wave is None else valu_per_wave * waves,
+                         "wave_instructions_per_cu_per_clock":
+                             None if valu_per_wave is None else valu_per_wave * waves / (ms / 1e3) / (256 * 2.4e9),
+                         "peak": 2.0,
+                         "fma_probe": valu_ceiling(sq, torch, dev)}},
         "wall_s_timed": wall,
     }
     if not args.no_extras:

@@ -227,6 +227,17 @@ sq_status sq_fp32_step(int32_t form, int32_t n_heads, int32_t dim_k, int32_t dim
                        const float* d_gate, const float* d_beta, float* d_y, void* stream);
 /* Streaming copy of n_bytes (multiple of 16, 16-byte aligned) for measuring achievable HBM bandwidth. */
 sq_status sq_copy(const void* d_src, void* d_dst, size_t n_bytes, void* stream);
+/* VALU issue-rate probe for measuring the instruction-issue ceiling of the step's occupancy:
+ * n_blocks workgroups of 256 threads (4 wave64, one per SIMD), each lane running 8 independent
+ * chains of 1024 fp32 FMAs, with dynamic LDS reserved so that at most waves_per_simd (1..8)
+ * workgroups, i.e. waves per SIMD, are resident on a CU.  d_out (device, caller-owned) receives
+ * n_blocks * 256 floats (the chains' sums).  On return *n_fma holds the wave-level FMA
+ * instructions the launch issues (n_blocks * 4 * 8192) and *blocks_per_cu the residency the
+ * runtime reports for that LDS reservation; time the launch on `stream` with events.
+ * SQ_ERR_ARG for NULL pointers or out-of-range sizes; SQ_ERR_UNSUPPORTED when the device's LDS
+ * cannot cap residency at waves_per_simd (the per-workgroup LDS limit); asynchronous otherwise. */
+sq_status sq_valu_probe(int32_t waves_per_simd, int32_t n_blocks, float* d_out, uint64_t* n_fma,
+                        int32_t* blocks_per_cu, void* stream);
 
 /* ---- errors / info ------------------------------------------------------ */
 const char* sq_status_str(sq_status s);

@@ -9,7 +9,7 @@ C++ runtime; there is no Python or CPU fallback.
 from __future__ import annotations
 
 import ctypes
-from ctypes import POINTER, byref, c_double, c_float, c_int32, c_size_t, c_void_p
+from ctypes import POINTER, byref, c_double, c_float, c_int32, c_size_t, c_uint64, c_void_p
 
 import numpy as np
 
@@ -20,7 +20,7 @@ from ._lib import (SQ_FORM_GDN, SQ_FORM_KDA, SQ_PIVOT_BITS, SQ_QUANT_DUAL_AXIS, 
 __all__ = [
     "StepQError", "Plan", "Pool", "sq_plan_create", "sq_plan_describe", "sq_plan_units", "sq_plan_rows",
     "sq_plan_save", "sq_plan_load", "sq_calib_generate", "sq_pool_bytes", "sq_pool_create", "sq_state_step",
-    "sq_pack", "sq_unpack", "sq_export", "sq_import", "sq_int8_step", "sq_fp32_step", "sq_copy",
+    "sq_pack", "sq_unpack", "sq_export", "sq_import", "sq_int8_step", "sq_fp32_step", "sq_copy", "sq_valu_probe",
     "sq_supported_shapes", "SQ_FORM_GDN", "SQ_FORM_KDA", "SQ_UNIT_HEAD", "SQ_UNIT_ROW", "SQ_STEP_SPLIT",
     "SQ_STEP_VALIDATE", "SQ_STEP_NO_JOIN", "SQ_PIVOT_BITS", "SQ_QUANT_DUAL_AXIS", "SQ_QUANT_ROW_ABSMAX",
 ]
@@ -337,3 +337,17 @@ def sq_copy(src, dst, n_bytes=None, stream=None):
     if src.numel() * src.element_size() < nb or dst.numel() * dst.element_size() < nb:
         raise ValueError("copy larger than the tensors")
     _check(_lib.load().sq_copy(c_void_p(src.data_ptr()), c_void_p(dst.data_ptr()), nb, _stream(stream)), "sq_copy")
+
+
+def sq_valu_probe(waves_per_simd, out, stream=None):
+    """Launch the FMA issue-rate probe over out.numel() // 256 workgroups (out: float32 on the GPU).
+    Returns (wave-level FMA instructions issued, workgroups resident per CU)."""
+    import torch
+    n_blocks = out.numel() // 256
+    if out.dtype != torch.float32 or not out.is_cuda or n_blocks < 1:
+        raise ValueError("out must be a float32 GPU tensor of at least 256 elements")
+    n = c_uint64(0)
+    fit = c_int32(0)
+    _check(_lib.load().sq_valu_probe(int(waves_per_simd), n_blocks, c_void_p(out.data_ptr()), byref(n), byref(fit),
+                                     _stream(stream)), "sq_valu_probe")
+    return n.value, fit.value

@@ -71,6 +71,7 @@ _SIGS = {
     "sq_fp32_step": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sq_copy": (c_int32, [_P, _P, c_size_t, _P]),
+    "sq_valu_probe": (c_int32, [c_int32, c_int32, _P, _P, _P, _P]),
     "sq_status_str": (ctypes.c_char_p, [c_int32]),
     "sq_last_error": (ctypes.c_char_p, []),
     "sq_supported_shapes": (c_int32, [POINTER(c_int32), c_int32]),

@@ -16,7 +16,7 @@ OUT = os.path.join(HERE, "libstepq.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 ARCH = os.environ.get("STEPQ_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "planner.cpp", "kernels.hip"]
+SOURCES = ["api.cpp", "planner.cpp", "kernels.hip", "probe.hip"]
 
 
 def _hipcc() -> str:

@@ -597,3 +597,23 @@ extern "C" sq_status sq_copy(const void* d_src, void* d_dst, size_t n_bytes, voi
     hipError_t e = launch_copy(d_src, d_dst, n_bytes, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SQ_OK : hip_fail(e, "copy launch");
 }
+
+extern "C" sq_status sq_valu_probe(int32_t waves_per_simd, int32_t n_blocks, float* d_out, uint64_t* n_fma,
+                                   int32_t* blocks_per_cu, void* stream) {
+    if (!d_out || !n_fma || !blocks_per_cu) { set_error("NULL pointer"); return SQ_ERR_ARG; }
+    if (waves_per_simd < 1 || waves_per_simd > 8 || n_blocks < 1) {
+        set_error("waves_per_simd must be in [1, 8] and n_blocks positive");
+        return SQ_ERR_ARG;
+    }
+    int fit = 0;
+    uint64_t n = 0;
+    hipError_t e = launch_valu_probe(waves_per_simd, n_blocks, d_out, &n, &fit, static_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidValue) {
+        set_error("this device's LDS cannot cap residency at that many waves per SIMD");
+        return SQ_ERR_UNSUPPORTED;
+    }
+    if (e != hipSuccess) return hip_fail(e, "VALU probe launch");
+    *n_fma = n;
+    *blocks_per_cu = fit;
+    return SQ_OK;
+}

@@ -19,6 +19,7 @@ hipError_t launch_codec(int, int, bool, const CodecParams&, int, hipStream_t) { 
 hipError_t launch_cmp(int, int, bool, int, int, int, int, int, int, const int32_t*, int8_t*, float*, float*,
                       const float*, const float*, const float*, const float*, const float*, float*, hipStream_t) { abort(); }
 hipError_t launch_copy(const void*, void*, size_t, hipStream_t) { abort(); }
+hipError_t launch_valu_probe(int, int, float*, uint64_t*, int*, hipStream_t) { abort(); }
 }
 
 static int fails = 0;

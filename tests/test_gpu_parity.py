@@ -615,6 +615,27 @@ def test_copy_kernel(torch):
     assert torch.equal(c[:n // 4], a[:n // 4]) and not bool(torch.any(c[n // 4:] != 0))
 
 
+def test_valu_probe(torch):
+    """The issue-rate probe caps residency at the requested waves per SIMD, reports the FMAs it issues,
+    and every lane's chains reach the affine recurrence's closed form."""
+    import quantized_delta_rule_02_amd as sq
+    n_blocks = 512
+    out = torch.full((n_blocks * 256,), float("nan"), device="cuda")
+    n_fma, fit = sq.sq_valu_probe(4, out)
+    torch.cuda.synchronize()
+    assert fit == 4 and n_fma == n_blocks * 4 * 1024 * 8
+    m, a = float(np.float32(0.999)), float(np.float32(0.001))
+    fix = a / (1.0 - m)
+    x0 = np.arange(256)[:, None] + np.arange(8)[None, :]
+    want = (fix + (x0 - fix) * m ** 1024).sum(axis=1)
+    got = out.cpu().numpy().reshape(n_blocks, 256)
+    assert np.all(np.isfinite(got))
+    assert np.allclose(got, want[None, :], rtol=1e-3)
+    n8, fit8 = sq.sq_valu_probe(8, out)
+    torch.cuda.synchronize()
+    assert fit8 == 8 and n8 == n_fma
+
+
 def test_validate_mode_rejects_bad_slots(torch):
     import quantized_delta_rule_02_amd as sq
     wl = configs.TINY

@@ -168,6 +168,11 @@ def test_argument_validation_status_codes():
     assert lib.sq_state_step(None, 0, 1, 1, None, None, None, None, None, None, None, None, None, 0) == -1
     assert lib.sq_pack(None, 0, 1, 1, None, None, None) == -1
     assert lib.sq_copy(None, None, 16, None) == -1
+    n_fma, fit = ctypes.c_uint64(0), ctypes.c_int32(0)
+    assert lib.sq_valu_probe(4, 1, None, ctypes.byref(n_fma), ctypes.byref(fit), None) == -1
+    for waves, blocks in ((0, 1), (9, 1), (4, 0)):
+        assert lib.sq_valu_probe(waves, blocks, ctypes.c_void_p(0x10000), ctypes.byref(n_fma), ctypes.byref(fit),
+                                 None) == -1
     assert lib.sq_int8_step(0, 32, 96, 128, 4, 0, 1, 1, None, None, None, None, None, None, None, None, None,
                             None) == -3
     # comparator state arrays: INT8 codes 16-byte aligned (one access per lane and group), FP32 states
