@@ -608,7 +608,7 @@ extern "C" sq_status sq_valu_probe(int32_t waves_per_simd, int32_t n_blocks, flo
     int fit = 0;
     uint64_t n = 0;
     hipError_t e = launch_valu_probe(waves_per_simd, n_blocks, d_out, &n, &fit, static_cast<hipStream_t>(stream));
-    if (e == hipErrorInvalidValue) {
+    if (e == hipErrorNotSupported) {
         set_error("this device's LDS cannot cap residency at that many waves per SIMD");
         return SQ_ERR_UNSUPPORTED;
     }

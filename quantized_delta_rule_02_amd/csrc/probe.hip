@@ -41,7 +41,7 @@ hipError_t launch_valu_probe(int waves_per_simd, int n_blocks, float* out, uint6
     if (e != hipSuccess) return e;
     // waves_per_simd workgroups fit in the CU's LDS, one more does not
     const size_t lds = (size_t(lds_cu) / size_t(waves_per_simd)) & ~size_t(1023);
-    if (lds == 0 || lds > size_t(lds_block) || (waves_per_simd + 1) * lds <= size_t(lds_cu)) return hipErrorInvalidValue;
+    if (lds == 0 || lds > size_t(lds_block) || (waves_per_simd + 1) * lds <= size_t(lds_cu)) return hipErrorNotSupported;
     int fit = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, k_valu_probe, kProbeThreads, lds);
     if (e != hipSuccess) return e;
