@@ -563,8 +563,8 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
         const float4 f = sm.fit[rbase + r];
         const float sw = f.y, nsw = f.z, hq = f.w;
         // The error is odd in t and round-half-even is symmetric, so the fit works on |t| (a free
-        // source modifier).  The first candidate of a round that starts at gamma = 1 cannot clip and
-        // skips the max.  The row's KG x CPL chains advance in stages separated by empty asm
+        // source modifier).  The first candidate of a round that starts at gamma = 1 cannot clip (the
+        // caller checks that no column base exceeds the binary16 range) and skips the max.  The row's KG x CPL chains advance in stages separated by empty asm
         // statements: left alone, the scheduler runs each chain to its end before the next, and a
         // wave then stalls on every dependent step.
         float t[CPL], A[KG][CPL], E[KG][CPL];
@@ -967,9 +967,14 @@ k_state(StepParams a) {
     }
     if ((hflags & kHasCodeRows) && a.quant_mode == 0) {   // per-row absmax keeps every column scale at 1
         const int n_grid = a.n_grid;
-        // with gamma = 1 no code can leave its range (|X / r| <= qmax c0 and the stored c rounds c0),
-        // so the first round skips the clamp of its first candidate when grid[0] == 1
-        if (a.unit_first) grid_round<Sh, KG, true>(sm, X, c0, a.grid, 0, n_grid, wave, lane, act, cbest, fbest);
+        // with gamma = 1 no code can leave its range (|X / r| <= qmax c0 and the stored c is c0 rounded to
+        // binary16, at most 2^-11 below it), so the first round skips the clamp of its first candidate when
+        // grid[0] == 1 -- unless a column base exceeds the largest binary16 scale, which the stored c is
+        // clamped to.  c0 is the workgroup's column maximum, so every wave takes the same branch.
+        bool sat = false;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sat = sat || c0[c] > 65504.f;
+        if (a.unit_first && !__any(sat)) grid_round<Sh, KG, true>(sm, X, c0, a.grid, 0, n_grid, wave, lane, act, cbest, fbest);
         else grid_round<Sh, KG, false>(sm, X, c0, a.grid, 0, n_grid, wave, lane, act, cbest, fbest);
         for (int g0 = KG; g0 < n_grid; g0 += KG) {
             __syncthreads();   // every wave has read the previous round's partials

@@ -74,7 +74,12 @@ def step_error_bound(P0: quant.Packed, rows: quant.RowPlan, k, v, alpha, beta, b
 
 
 def _spacing16(x):
-    return np.spacing(np.abs(np.asarray(x, np.float64)).astype(np.float16)).astype(np.float64)
+    """Gap from |x| (a binary16 value) to its binary16 neighbour above; at the largest finite value, 65504,
+    the gap below (32), since above it lies infinity."""
+    h = np.abs(np.asarray(x, np.float64)).astype(np.float16)
+    top = h == np.float16(65504)
+    up = np.spacing(np.where(top, np.float16(0), h))
+    return np.where(top, 32.0, up.astype(np.float64))
 
 
 def _fp16_neighbours_tie(pre, got, want, tol):

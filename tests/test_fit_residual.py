@@ -58,8 +58,9 @@ def test_residual_matches_the_clamped_rounding(bits):
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
 def test_first_candidate_needs_no_clamp(bits):
-    """gamma = 1: c is the binary16 rounding of c0 = max |X| / (r qmax), at most 2^-11 below it,
-    so y <= qmax (1 + 2^-11) < qmax + 1/2 and the fract alone is the residual."""
+    """gamma = 1: c is the binary16 rounding of c0 = max |X| / (r qmax), at most 2^-11 below it while
+    c0 <= 65504, so y <= qmax (1 + 2^-11) < qmax + 1/2 and the fract alone is the residual.  (Above
+    65504 the stored scale is clamped and the kernel uses the clamping form for gamma = 1 as well.)"""
     qmax = 2 ** (bits - 1) - 1
     ymax = qmax * (1.0 + 2.0 ** -11)
     assert ymax < qmax + 0.5

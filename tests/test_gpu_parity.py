@@ -172,6 +172,32 @@ def _degenerate_states(rig, seed):
 
 
 @pytest.mark.parametrize("wl", [configs.GDN_DECODE, configs.KDA_DECODE], ids=["gdn", "kda"])
+def test_saturating_column_scales(torch, wl):
+    """States so large that row factors saturate at the binary16 maximum and column bases c0 spread over
+    five decades around it: where c0 exceeds 65504 the first candidate's scale is clamped below c0, its
+    codes clip, and the fit must count the clipped residuals (no shortcut for gamma = 1)."""
+    import quantized_delta_rule_02_amd as sq
+    say(f"saturating column scales {wl.name}")
+    rig = _rig(wl, 1, 1)
+    g = np.random.default_rng(23)
+    s = 10.0 ** g.uniform(9.0, 13.0, (rig.N, 1, rig.dv))
+    X = s * g.uniform(-1.0, 1.0, (rig.N, rig.dk, rig.dv))
+    rows = g.integers(0, rig.dk, (rig.N, rig.dv))
+    n, j = np.meshgrid(np.arange(rig.N), np.arange(rig.dv), indexing="ij")
+    X[n, rows, j] = s[:, 0, :] * np.where(g.random((rig.N, rig.dv)) < 0.5, -1.0, 1.0)
+    X = X.astype(np.float32).astype(np.float64)
+    c0 = quant.column_base(X, rig.rows, quant.row_factors(X, rig.rows)[1])
+    assert np.count_nonzero((c0 > 65504 * 1.02) & (c0 < 65504 / 0.875)) >= 10   # the clipping window is hit
+    sq.sq_pack(rig.pool, 0, 1, 1, rig.slots, rig._t(X.reshape(-1), torch.float32))
+    torch.cuda.synchronize()
+    zeros = np.zeros((rig.N, rig.dv))
+    R = compare_step(X, zeros, rig.rows, wl.grid, zeros, rig.export_packed(), quant.quantize(X, rig.rows, wl.grid))
+    say(R)
+    assert R.ok(), R.failures
+    rig.close()
+
+
+@pytest.mark.parametrize("wl", [configs.GDN_DECODE, configs.KDA_DECODE], ids=["gdn", "kda"])
 def test_degenerate_states_pack_and_step(torch, wl):
     """Zero states, zero rows and columns, clamped scales, rank-one and single-entry states: pack, one step
     with the workload's inputs, and one step with alpha = 1, beta = 0 (the update is the identity, so the

@@ -113,3 +113,17 @@ def test_compare_in_row_absmax_mode():
     assert not compare_step(X, y, rows, grid, y.copy(), bad, P2, mode="row_absmax").ok()
     # the dual-axis comparison rejects a row-absmax result (different row factors)
     assert not compare_step(X, y, rows, grid, y.copy(), P2, P2).ok()
+
+
+def test_binary16_neighbours_at_the_top_of_the_range():
+    """Adjacent binary16 values are accepted as a rounding tie only when the pre-rounding value sits at
+    their midpoint; at 65504, whose upper neighbour is infinity, the gap is the one below (32)."""
+    from _parity import _fp16_neighbours_tie, _spacing16
+    assert _spacing16(np.array([65504.0]))[0] == 32.0
+    assert _spacing16(np.array([1.0]))[0] == 2.0 ** -10
+    assert _spacing16(np.array([65472.0]))[0] == 32.0
+    got, want = np.array([65504.0]), np.array([65472.0])
+    assert _fp16_neighbours_tie(np.array([65488.0]), got, want, 1e-5)[0]
+    assert not _fp16_neighbours_tie(np.array([65500.0]), got, want, 1e-5)[0]
+    # not neighbours: the largest value against one far below it
+    assert not _fp16_neighbours_tie(np.array([32768.0]), np.array([65504.0]), np.array([1024.0]), 1.0)[0]
