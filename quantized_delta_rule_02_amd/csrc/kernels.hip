@@ -612,7 +612,9 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
 #pragma unroll
             for (int w = 0; w < NW; ++w) F += act ? sm.part[w][j][col0 + c] : 0.f;
             F *= cg[j][c] * cg[j][c];
-            if (F < fbest[c]) {
+            // the grid's first candidate is taken unconditionally, so an objective that overflows
+            // (states beyond about 1e17 / sqrt(w)) still leaves a candidate of the grid, not the initial 1
+            if ((g0 == 0 && j == 0) || F < fbest[c]) {
                 fbest[c] = F;
                 cbest[c] = cg[j][c];
             }
