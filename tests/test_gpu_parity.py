@@ -673,3 +673,41 @@ def test_validate_mode_rejects_bad_slots(torch):
             rig.step(q[0], k[0], v[0], beta[0], flags=sq.SQ_STEP_VALIDATE)
         assert e.value.status == -4
     rig.close()
+
+
+SWEEP = [("gdn", configs.GDN_DECODE, 1, 2), ("kda", configs.KDA_DECODE, 1, 2), ("serving6", configs.SERVING_6, 2, 1),
+         ("serving4-mixed", configs.SERVING_4_MIXED, 2, 1), ("outlier", configs.OUTLIER, 1, 1),
+         ("outlier-mixed", configs.OUTLIER_MIXED, 1, 1), ("gdn64", configs.GDN_64, 1, 2), ("kda64", configs.KDA_64, 1, 2)]
+
+
+@pytest.mark.parametrize("name,wl,nL,B", SWEEP, ids=[c[0] for c in SWEEP])
+def test_seeded_sweep(torch, name, wl, nL, B):
+    """Pack and one teacher-forced step over six seeds: the warmed-up states perturbed entry by entry and
+    rescaled per state by 1e-3 .. 1e3, inputs from six sub-streams of the workload's generator."""
+    import quantized_delta_rule_02_amd as sq
+    say(f"seeded sweep {name}")
+    rig = _rig(wl, nL, B)
+    S0 = rig.warm_state(steps=min(wl.warmup_steps, 64))
+    ties = 0
+    for seed in range(6):
+        g = np.random.default_rng(1000 + seed)
+        scale = 10.0 ** g.uniform(-3, 3, (rig.N, 1, 1))
+        S = (S0 * (1 + 0.3 * g.standard_normal(S0.shape)) + 0.1 * np.abs(S0).mean() * g.standard_normal(S0.shape))
+        S = (S * scale).astype(np.float32).astype(np.float64)
+        sq.sq_pack(rig.pool, 0, nL, B, rig.slots, rig._t(S.reshape(-1), torch.float32))
+        torch.cuda.synchronize()
+        z = np.zeros((rig.N, rig.dv))
+        P = quant.quantize(S, rig.rows, wl.grid)
+        R = compare_step(S, z, rig.rows, wl.grid, z, rig.export_packed(), P)
+        assert R.ok(), (seed, "pack", R.failures)
+        q, k, v, beta = rig.inputs(1, sub=seed + 1)
+        alpha = rig.alpha_states()
+        rig.import_packed(P)
+        y_g = rig.step(q[0], k[0], v[0], beta[0])
+        P2, y, Xo = packed_step(P, rig.rows, q[0], k[0], v[0], alpha, beta[0], wl.grid)
+        R2 = compare_step(Xo, y, rig.rows, wl.grid, y_g, rig.export_packed(), P2,
+                          x_err=step_error_bound(P, rig.rows, k[0], v[0], alpha, beta[0]))
+        assert R2.ok(), (seed, "step", R2.failures)
+        ties += R.fit_ties + R2.fit_ties
+    say(f"  column-scale choices other than the oracle's argmin: {ties}")
+    rig.close()
