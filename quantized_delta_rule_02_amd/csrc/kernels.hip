@@ -524,10 +524,11 @@ __device__ __forceinline__ void round_pack_uniform(const float* X, const float* 
 //
 // The residual y - Q of y = |t| / c >= 0 and Q = min(rint(y), qmax) comes without forming Q:
 // with a = y + 1/2 - qmax (one FMA; qmax is an integer, so fract(a) = fract(y + 1/2)),
-//   y <= qmax + 1/2:  a <= 1 and fract(a) - 1/2 = y - round(y), and fract(a) >= a;
+//   y <  qmax + 1/2:  a < 1 and fract(a) - 1/2 = y - round(y), and fract(a) >= a;
 //   y >  qmax + 1/2:  a > 1, the code clips to qmax and the residual is y - qmax = a - 1/2 > fract(a) - 1/2;
-// so y - Q = max(a, fract(a)) - 1/2 in both cases (at an exact half-way point either rounding leaves
-// the same squared residual).  Per candidate and entry: FMA, fract, max, the weight FMA and the
+//   y == qmax + 1/2:  a = 1, a half-way point: max(a, fract(a)) - 1/2 = 1/2, the residual of either rounding;
+// so |y - Q| = |max(a, fract(a)) - 1/2| in every case (at any half-way point either rounding leaves the
+// same squared residual).  Per candidate and entry: FMA, fract, max, the weight FMA and the
 // accumulating FMA.  a carries the rounding of a sum of magnitude up to qmax, about 2^-24 qmax,
 // the order of the float32 error that t itself already has.
 template <class Sh, int KG, bool FREE0, class Smem>
