@@ -172,6 +172,31 @@ def _degenerate_states(rig, seed):
 
 
 @pytest.mark.parametrize("wl", [configs.GDN_DECODE, configs.KDA_DECODE], ids=["gdn", "kda"])
+def test_extreme_gates_and_inputs(torch, wl):
+    """One step with gates across the domain (1, 0.5, 1e-6, 1e-30: a state decayed to almost nothing), beta
+    0, 1/2 or 1, and values v scaled up to 1e6: the update, readout and requantization follow the oracle."""
+    say(f"extreme gates {wl.name}")
+    rig = _rig(wl, 1, 1)
+    S0 = rig.warm_state(steps=min(wl.warmup_steps, 64))
+    P = quant.quantize(S0, rig.rows, wl.grid)
+    g = np.random.default_rng(31)
+    rig.gates = g.choice(np.array([1.0, 0.5, 1e-6, 1e-30]), size=rig.gates.shape).astype(np.float32)
+    alpha = rig.alpha_states()
+    q, k, v, beta = rig.inputs(1)
+    beta = g.choice(np.array([0.0, 0.5, 1.0]), size=beta.shape)
+    v = v * (10.0 ** g.choice(np.array([0.0, 3.0, 6.0]), size=(1, rig.N, 1)))
+    v = v.astype(np.float32).astype(np.float64)
+    rig.import_packed(P)
+    y_g = rig.step(q[0], k[0], v[0], beta[0])
+    P2, y, Xo = packed_step(P, rig.rows, q[0], k[0], v[0], alpha, beta[0], wl.grid)
+    R = compare_step(Xo, y, rig.rows, wl.grid, y_g, rig.export_packed(), P2,
+                     x_err=step_error_bound(P, rig.rows, k[0], v[0], alpha, beta[0]))
+    say(R)
+    assert R.ok(), R.failures
+    rig.close()
+
+
+@pytest.mark.parametrize("wl", [configs.GDN_DECODE, configs.KDA_DECODE], ids=["gdn", "kda"])
 def test_saturating_column_scales(torch, wl):
     """States so large that row factors saturate at the binary16 maximum and column bases c0 spread over
     five decades around it: where c0 exceeds 65504 the first candidate's scale is clamped below c0, its
