@@ -31,6 +31,10 @@
  *     unspecified, never memory outside them.
  *   - A call over an empty range (batch = 0 or n_layers = 0) validates its
  *     sizes and returns SQ_OK without touching any array (they may be NULL).
+ *   - Host threads: a plan is read-only after creation and may be shared; calls
+ *     on one pool may come from several threads (the split arrangement
+ *     serializes its own set-up per pool).  Device work that touches the same
+ *     slots must still be ordered by the caller (streams, events).
  *   - Every call validates its arguments on the host before enqueuing work and
  *     returns a negative sq_status on failure, with a message available from
  *     sq_last_error() on the calling thread.  Device work is asynchronous: a

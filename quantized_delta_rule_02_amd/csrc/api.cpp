@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -54,6 +55,7 @@ struct sq_pool {
     float* e_buf = nullptr;          // split arrangement scratch (v - k^T D S per state)
     size_t e_cap = 0;                // floats
     std::vector<hipEvent_t> events;  // split arrangement: one per chunk
+    std::mutex split_mu;             // serializes the split arrangement's lazy set-up and event use
 };
 
 // ------------------------------------------------------------------ errors / info
@@ -446,6 +448,9 @@ extern "C" sq_status sq_state_step(sq_pool* pl, int32_t layer0, int32_t n_layers
     // split arrangement: per chunk, readout kernel on the main stream, fit + pack on the aux stream.
     // Scratch e = v - k^T D S: one region per (layer, request index, head), allocated once per pool.
     const int64_t layer_stride = int64_t(pl->n_slots) * pl->H;
+    // host threads that enqueue split steps on one pool take turns (the scratch is allocated on first
+    // use and the chunk events are shared); the device work itself is ordered by the streams and events
+    std::lock_guard<std::mutex> lock(pl->split_mu);
     if (!pl->e_buf) {
         const size_t need = size_t(pl->L) * size_t(layer_stride) * pl->dv;
         e = hipMalloc(reinterpret_cast<void**>(&pl->e_buf), need * sizeof(float));

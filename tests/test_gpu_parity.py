@@ -443,6 +443,55 @@ def test_split_without_join_per_layer_equals_fused(torch):
     rig.close()
 
 
+def test_split_from_two_host_threads(torch):
+    """Two host threads enqueue split steps on one pool at once, one layer each on streams of their own
+    (the library serializes the split arrangement's set-up per pool): bytes and readout equal one fused
+    call over both layers."""
+    import threading
+    import quantized_delta_rule_02_amd as sq
+    wl = configs.SERVING_6
+    nL, B = 2, 2
+    say("split from two host threads serving6")
+    rig = _rig(wl, nL, B)
+    P = quant.quantize(rig.warm_state(steps=32), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(1)
+    per, dk, dv = B * rig.H, rig.dk, rig.dv
+    t = lambda a: rig._t(np.ascontiguousarray(a).reshape(-1), torch.float32)
+    qs, ks, vs, bs, gate = t(q[0]), t(k[0]), t(v[0]), t(beta[0]), rig.gate_step()
+    rig.import_packed(P)
+    y_ref = torch.zeros(rig.N * dv, dtype=torch.float32, device="cuda")
+    sq.sq_state_step(rig.pool, 0, nL, B, rig.slots, qs, ks, vs, gate, bs, y_ref)
+    torch.cuda.synchronize()
+    mem_ref = rig.mem.clone()
+    for _ in range(3):
+        rig.import_packed(P)
+        y = torch.zeros(rig.N * dv, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        errors = []
+
+        def worker(l):
+            try:
+                main, aux = torch.cuda.Stream(), torch.cuda.Stream()
+                a0, a1 = l * per, (l + 1) * per
+                sq.sq_state_step(rig.pool, l, 1, B, rig.slots, qs[a0 * dk:a1 * dk], ks[a0 * dk:a1 * dk],
+                                 vs[a0 * dv:a1 * dv], gate[a0:a1], bs[a0:a1], y[a0 * dv:a1 * dv],
+                                 stream_main=main, stream_aux=aux, flags=sq.SQ_STEP_SPLIT)
+                main.synchronize()
+            except Exception as e:      # reported below, in the test's own thread
+                errors.append(e)
+
+        threads = [threading.Thread(target=worker, args=(l,)) for l in range(nL)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+        torch.cuda.synchronize()
+        assert not errors, errors
+        assert torch.equal(y, y_ref)
+        assert torch.equal(rig.mem, mem_ref)
+    rig.close()
+
+
 def test_fused_step_replays_in_a_hip_graph(torch):
     """The fused step captured once in a HIP graph and replayed: every replay, with eager work and
     synchronizations between replays, equals the eager step on the same inputs (bytes and readout)."""
