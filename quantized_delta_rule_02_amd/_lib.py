@@ -4,7 +4,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
-from ctypes import POINTER, c_double, c_float, c_int16, c_int32, c_int8, c_size_t, c_uint16, c_uint32, c_uint64, c_void_p
+from ctypes import POINTER, c_double, c_float, c_int32, c_size_t, c_uint32, c_uint64, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libstepq.so")

@@ -12,7 +12,7 @@ from oracle.numerics import fp16_round
 from oracle.step import packed_step, run_packed
 from workloads import configs, gen
 
-from _parity import compare_step, from_canonical, step_error_bound, to_canonical
+from _parity import compare_step, step_error_bound
 
 pytestmark = pytest.mark.gpu
 
