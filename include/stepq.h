@@ -154,6 +154,13 @@ sq_status sq_pool_bytes(const sq_plan* plan, int32_t n_slots, size_t* bytes);
 sq_status sq_pool_create(const sq_plan* plan, void* d_pool, size_t pool_bytes, int32_t n_slots,
                          sq_pool** out);
 void      sq_pool_destroy(sq_pool* pool);
+/* The same three calls under the names the method's decode-step interface is usually described
+ * with: sq_plan_info = sq_plan_describe, sq_pool_bind = sq_pool_create (the caller's device buffer
+ * is bound, not allocated), sq_pool_release = sq_pool_destroy. */
+sq_status sq_plan_info(const sq_plan* plan, sq_plan_desc* out);
+sq_status sq_pool_bind(const sq_plan* plan, void* d_pool, size_t pool_bytes, int32_t n_slots,
+                       sq_pool** out);
+void      sq_pool_release(sq_pool* pool);
 
 #define SQ_STEP_SPLIT    1u       /* two kernels: readout on stream_main, fit + pack on stream_aux */
 #define SQ_STEP_VALIDATE 2u       /* copy the slot list to the host and check range and uniqueness */

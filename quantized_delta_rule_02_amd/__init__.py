@@ -18,7 +18,7 @@ from ._lib import (SQ_FORM_GDN, SQ_FORM_KDA, SQ_PIVOT_BITS, SQ_QUANT_DUAL_AXIS, 
                    SQ_STEP_NO_JOIN, SQ_STEP_SPLIT, SQ_STEP_VALIDATE, SQ_UNIT_HEAD, SQ_UNIT_ROW)
 
 __all__ = [
-    "StepQError", "Plan", "Pool", "sq_plan_create", "sq_plan_describe", "sq_plan_units", "sq_plan_rows",
+    "StepQError", "Plan", "Pool", "sq_plan_create", "sq_plan_describe", "sq_plan_info", "sq_pool_bind", "sq_pool_release", "sq_plan_units", "sq_plan_rows",
     "sq_plan_save", "sq_plan_load", "sq_calib_generate", "sq_pool_bytes", "sq_pool_create", "sq_state_step",
     "sq_pack", "sq_unpack", "sq_export", "sq_import", "sq_int8_step", "sq_fp32_step", "sq_copy", "sq_valu_probe",
     "sq_supported_shapes", "SQ_FORM_GDN", "SQ_FORM_KDA", "SQ_UNIT_HEAD", "SQ_UNIT_ROW", "SQ_STEP_SPLIT",
@@ -127,12 +127,17 @@ def sq_plan_create(*, form, unit, n_layers, n_heads, d_k, d_v, widths, budget_mi
     return Plan(out.value)
 
 
-def sq_plan_describe(plan: Plan) -> dict:
+def sq_plan_describe(plan: Plan, _entry="sq_plan_describe") -> dict:
     d = _lib.SqPlanDesc()
-    _check(_lib.load().sq_plan_describe(plan.handle, byref(d)), "sq_plan_describe")
+    _check(getattr(_lib.load(), _entry)(plan.handle, byref(d)), _entry)
     out = {name: getattr(d, name) for name, _ in d._fields_}
     out["widths"] = [int(d.widths[i]) for i in range(d.n_widths)]
     return out
+
+
+def sq_plan_info(plan: Plan) -> dict:
+    """sq_plan_describe under its other name (the C ABI exports both)."""
+    return sq_plan_describe(plan, _entry="sq_plan_info")
 
 
 def sq_plan_units(plan: Plan) -> dict:
@@ -248,14 +253,26 @@ def sq_pool_bytes(plan: Plan, n_slots: int) -> int:
     return n.value
 
 
-def sq_pool_create(plan: Plan, memory, n_slots: int) -> Pool:
+def sq_pool_create(plan: Plan, memory, n_slots: int, _entry="sq_pool_create") -> Pool:
     """memory: a uint8 CUDA tensor of at least sq_pool_bytes(plan, n_slots) bytes."""
     import torch
     nbytes = sq_pool_bytes(plan, n_slots)
     ptr = _dev(memory, torch.uint8, nbytes, "pool memory")
     out = c_void_p()
-    _check(_lib.load().sq_pool_create(plan.handle, ptr, memory.numel(), n_slots, byref(out)), "sq_pool_create")
+    _check(getattr(_lib.load(), _entry)(plan.handle, ptr, memory.numel(), n_slots, byref(out)), _entry)
     return Pool(out.value, plan, memory, n_slots)
+
+
+def sq_pool_bind(plan: Plan, memory, n_slots: int) -> Pool:
+    """sq_pool_create under its other name (the C ABI exports both): binds caller-owned memory."""
+    return sq_pool_create(plan, memory, n_slots, _entry="sq_pool_bind")
+
+
+def sq_pool_release(pool: Pool) -> None:
+    """Release a pool's device tables (the C ABI's sq_pool_release); the caller's memory stays."""
+    if pool.handle and pool.handle.value:
+        _lib.load().sq_pool_release(pool.handle)
+        pool.handle = c_void_p(None)
 
 
 def sq_state_step(pool: Pool, layer0, n_layers, batch, slots, q, k, v, gate, beta, y,

@@ -61,6 +61,9 @@ _SIGS = {
     "sq_pool_bytes": (c_int32, [_P, c_int32, POINTER(c_size_t)]),
     "sq_pool_create": (c_int32, [_P, _P, c_size_t, c_int32, POINTER(c_void_p)]),
     "sq_pool_destroy": (None, [_P]),
+    "sq_plan_info": (c_int32, [_P, POINTER(SqPlanDesc)]),
+    "sq_pool_bind": (c_int32, [_P, _P, c_size_t, c_int32, POINTER(c_void_p)]),
+    "sq_pool_release": (None, [_P]),
     "sq_state_step": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_uint32]),
     "sq_pack": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P]),
     "sq_unpack": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P]),

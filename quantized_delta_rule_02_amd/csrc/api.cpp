@@ -622,3 +622,13 @@ extern "C" sq_status sq_valu_probe(int32_t waves_per_simd, int32_t n_blocks, flo
     *blocks_per_cu = fit;
     return SQ_OK;
 }
+
+// ------------------------------------------------------------------ alternative names
+
+extern "C" sq_status sq_plan_info(const sq_plan* p, sq_plan_desc* out) { return sq_plan_describe(p, out); }
+
+extern "C" sq_status sq_pool_bind(const sq_plan* p, void* d_pool, size_t pool_bytes, int32_t n_slots, sq_pool** out) {
+    return sq_pool_create(p, d_pool, pool_bytes, n_slots, out);
+}
+
+extern "C" void sq_pool_release(sq_pool* pl) { sq_pool_destroy(pl); }

@@ -700,6 +700,31 @@ def test_int8_and_fp32_comparators(torch, wl):
     assert np.array_equal(got_c[H:2 * H], codes[H:2 * H])            # slot 1 untouched
 
 
+def test_pool_bind_and_release(torch):
+    """A pool bound through sq_pool_bind steps exactly like one from sq_pool_create over the same bytes;
+    sq_pool_release frees its tables and leaves the caller's memory."""
+    import quantized_delta_rule_02_amd as sq
+    wl = configs.GDN_DECODE
+    rig = _rig(wl, 1, 2)
+    P = quant.quantize(rig.warm_state(steps=16), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(1)
+    rig.import_packed(P)
+    mem0 = rig.mem.clone()
+    y_ref = rig.step(q[0], k[0], v[0], beta[0])
+    mem_ref = rig.mem.clone()
+    mem = mem0.clone()
+    pool = sq.sq_pool_bind(rig.plan, mem, rig.pool.n_slots)
+    y = torch.zeros(rig.N * rig.dv, dtype=torch.float32, device="cuda")
+    t = lambda a: rig._t(np.ascontiguousarray(a).reshape(-1), torch.float32)
+    sq.sq_state_step(pool, 0, 1, rig.B, rig.slots, t(q[0]), t(k[0]), t(v[0]), rig.gate_step(), t(beta[0]), y)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().reshape(rig.N, rig.dv), y_ref.astype(np.float32))
+    assert torch.equal(mem, mem_ref)
+    sq.sq_pool_release(pool)
+    assert torch.equal(mem, mem_ref)
+    rig.close()
+
+
 def test_copy_kernel(torch):
     import quantized_delta_rule_02_amd as sq
     a = torch.randn(1 << 20, device="cuda")

@@ -29,6 +29,19 @@ def test_library_exports_every_declared_function():
     assert set(names) <= exported
 
 
+def test_alternative_names_are_the_same_calls():
+    """sq_plan_info is sq_plan_describe; sq_pool_bind / sq_pool_release validate like sq_pool_create /
+    sq_pool_destroy (host checks only, no device memory)."""
+    wl = configs.GDN_DECODE
+    plan = sq.sq_plan_create(**_plan_kw(wl, 1))
+    assert sq.sq_plan_info(plan) == sq.sq_plan_describe(plan)
+    lib = _lib.load()
+    out = ctypes.c_void_p()
+    assert lib.sq_pool_bind(plan.handle, None, 16, 1, ctypes.byref(out)) == -1 and not out.value
+    lib.sq_pool_release(None)          # a NULL pool is ignored
+    plan.close()
+
+
 def test_supported_shapes_cover_the_workloads():
     shapes = set(sq.sq_supported_shapes())
     for w in configs.ALL:
