@@ -10,10 +10,14 @@ Sources
   error; every scaled entry then goes to the nearest representable level at
   its unit's precision.  The first paragraph of the same section fixes the
   quantizer as symmetric and uniform.
-* rcap.io post, decode-step pseudocode: row_scales = sqrt(row_mag) /
-  sqrt(row_impact_weight); col_scales = fit_weighted_lsq(X, row_scales, ...);
-  codes = quantize(X / (row_scales * col_scales), bits_per_unit); and
-  S_prev = unpack(codes, row_scales, col_scales, fp16_pivots).
+* rcap.io post, decode-step pseudocode: after the update, the row factors are
+  the square root of each row's magnitude over the square root of its impact
+  score, the column scales come from an impact-weighted least-squares fit given
+  those row factors, the codes are the state divided by the product of the two
+  scales and rounded at each unit's width, and the next step reconstructs the
+  state from codes, row factors, column scales and the binary16 pivots.  In
+  this module's notation: r_i = binary16(sqrt(m_i / w_i)), then the weighted
+  grid fit for c_j, then Q_ij = clamp(rint(X_ij / (r_i c_j))).
 * hyper.ai summary, 方法, the Lifetime-Aware Bit Allocation paragraph: the
   riskiest units are kept in FP16 as sparse pivots.
 

@@ -91,6 +91,56 @@ def _allocate_widest_first(cost, widths, budget_milli):
     return np.full(cost.shape[0], len(widths) - 1)
 
 
+_orig_head_distortion = planner.head_distortion
+
+
+def _distortion_weighted(snap, w_head, widths, grid, unit, mode="dual_axis"):
+    """Squared errors weighted by the impact score (the fit's objective instead of the plain reconstruction)."""
+    n_seg, d_k, _ = snap.shape
+    out = []
+    for b in widths:
+        rows = quant.RowPlan(bits=np.full((n_seg, d_k), b), pivot=np.zeros((n_seg, d_k), bool),
+                             w=np.broadcast_to(np.asarray(w_head, np.float64), (n_seg, d_k)))
+        err = snap - quant.dequantize(quant.quantize(snap, rows, grid, mode=mode), rows)
+        e2 = np.sum(err * err, axis=2) * np.asarray(w_head, np.float64)[None, :]
+        out.append(e2.sum(axis=1).mean()[None] if unit == "head" else e2.mean(axis=0))
+    return np.stack(out, axis=-1)
+
+
+def _distortion_first_row_pivot(snap, w_head, widths, grid, unit, mode="dual_axis"):
+    """The first key row treated as a pivot (excluded from the quantizer) while distortion is measured."""
+    n_seg, d_k, _ = snap.shape
+    piv = np.zeros((n_seg, d_k), bool)
+    piv[:, 0] = True
+    out = []
+    for b in widths:
+        rows = quant.RowPlan(bits=np.full((n_seg, d_k), b), pivot=piv,
+                             w=np.broadcast_to(np.asarray(w_head, np.float64), (n_seg, d_k)))
+        err = snap - quant.dequantize(quant.quantize(snap, rows, grid, mode=mode), rows)
+        e2 = np.sum(err * err, axis=2)
+        out.append(e2.sum(axis=1).mean()[None] if unit == "head" else e2.mean(axis=0))
+    return np.stack(out, axis=-1)
+
+
+def _distortion_next_width(snap, w_head, widths, grid, unit, mode="dual_axis"):
+    """Each column measured at the next wider candidate width (an index off by one)."""
+    ws = list(widths)
+    shifted = [ws[min(i + 1, len(ws) - 1)] for i in range(len(ws))]
+    return _orig_head_distortion(snap, w_head, shifted, grid, unit, mode)
+
+
+def _snapshots_drop_last_token(q, k, v, beta, alpha_head):
+    return _orig_snapshots(q[:, :-1], k[:, :-1], v[:, :-1], beta[:, :-1], alpha_head)
+
+
+def _snapshots_reset_per_token(q, k, v, beta, alpha_head):
+    """Each token starts again from the zero state (the recurrence is not carried)."""
+    return _orig_snapshots(q[:, -1:], k[:, -1:], v[:, -1:], beta[:, -1:], alpha_head)
+
+
+_orig_snapshots = planner.calib_snapshots
+
+
 CASES = [
     ("update sign", [(recurrence, "delta_update", _update_sign_flip), (tr, "delta_update", _update_sign_flip)],
      tr.test_write_property_unit_gate),
@@ -116,6 +166,16 @@ CASES = [
      tp.test_impact_score_is_the_readout_sensitivity),
     ("allocation ignores budget", [(planner, "allocate", _allocate_widest_first)],
      lambda: tp.test_allocation_equals_brute_force(1, 8, 6000)),
+    ("distortion weighted by impact", [(planner, "head_distortion", _distortion_weighted)],
+     tp.test_distortion_worked_example_2x2),
+    ("distortion with a pivot row excluded", [(planner, "head_distortion", _distortion_first_row_pivot)],
+     tp.test_distortion_worked_example_2x2),
+    ("distortion at the next width", [(planner, "head_distortion", _distortion_next_width)],
+     lambda: tp.test_distortion_equals_exact_brute_force_4x4(0)),
+    ("snapshot drops the last token", [(planner, "calib_snapshots", _snapshots_drop_last_token)],
+     tp.test_calibration_snapshot_three_tokens),
+    ("snapshot restarts per token", [(planner, "calib_snapshots", _snapshots_reset_per_token)],
+     tp.test_calibration_snapshot_three_tokens),
 ]
 
 

@@ -186,3 +186,187 @@ def test_make_plan_small_end_to_end():
     ref = _brute_alloc(p.L[rest, None] * p.D[rest], (4, 6, 8), 6000)
     assert np.array_equal(p.unit_bits[rest], np.asarray((4, 6, 8))[ref])
     assert np.all(p.bits[0, p.pivot_units] == 16) and np.all(p.pivot[0, p.pivot_units])
+
+
+# ---------------------------------------------------------------- distortion and calibration snapshots
+#
+# hyper.ai summary, 方法 (Method), the Lifetime-Aware Bit Allocation paragraph: the planner estimates each
+# unit's reconstruction distortion at every candidate width on calibration states.  Reading taken: D_u(b) is
+# the mean over the segment-final calibration states of the unweighted squared error of the unit's entries,
+# with every row of the state quantized at width b by the step's own quantizer and no row kept as a pivot.
+
+from fractions import Fraction as Fr
+from math import isqrt
+
+GRID4_EXACT = (Fr(1), Fr(7, 8), Fr(3, 4), Fr(5, 8))
+
+
+def _ulp16(x: Fr) -> Fr:
+    """Spacing of binary16 values around a positive x in the normal range (11 significant bits)."""
+    e = 0
+    while x >= Fr(2) ** (e + 1):
+        e += 1
+    while x < Fr(2) ** e:
+        e -= 1
+    return Fr(2) ** (max(e, -14) - 10)
+
+
+def _f16_exact(x: Fr) -> Fr:
+    """binary16 value nearest to a positive rational x (ties to even), clamped to [2^-14, 65504] first."""
+    x = min(max(x, Fr(1, 2 ** 14)), Fr(65504))
+    ulp = _ulp16(x)
+    n, rem = divmod(x, ulp)
+    n = int(n)
+    if rem > ulp / 2 or (rem == ulp / 2 and n % 2 == 1):
+        n += 1
+    return min(n * ulp, Fr(65504))
+
+
+def _f16_sqrt_exact(x: Fr) -> Fr:
+    """binary16 value nearest to sqrt(x) for a positive rational x, by comparing squares (exact)."""
+    num, den = x.numerator, x.denominator
+    s = Fr(isqrt(num * den), den)              # s <= sqrt(x) < s + 1/den
+    lo = min(max(s, Fr(1, 2 ** 14)), Fr(65504))
+    ulp = _ulp16(lo)
+    n = int(lo // ulp)
+    while ((n + 1) * ulp) ** 2 <= x:           # largest multiple of ulp whose square is <= x
+        n += 1
+    while n > 0 and (n * ulp) ** 2 > x:
+        n -= 1
+    mid = (n + Fr(1, 2)) * ulp
+    if mid * mid < x or (mid * mid == x and n % 2 == 1):
+        n += 1
+    return min(max(n * ulp, Fr(1, 2 ** 14)), Fr(65504))
+
+
+def _exact_state_error(X, w, b):
+    """Squared error per entry of the dual-axis quantizer at width b, in exact rational arithmetic: the row
+    factors from binary16(sqrt(m / w)), every candidate scale binary16(gamma c0), the codes of each candidate
+    found by trying every code in [-qmax, qmax], the candidate with the smallest impact-weighted error (first
+    on ties).  X is a list of rows of Fractions, w a list of Fractions."""
+    dk, dv = len(X), len(X[0])
+    qm = 2 ** (b - 1) - 1
+    r = []
+    for i in range(dk):
+        m = max(abs(x) for x in X[i])
+        r.append(Fr(1) if m == 0 else _f16_sqrt_exact(m / w[i]))
+    err = [[Fr(0)] * dv for _ in range(dk)]
+    for j in range(dv):
+        c0 = max(abs(X[i][j]) / (r[i] * qm) for i in range(dk))
+        if c0 == 0:
+            continue
+        best = None
+        for g in GRID4_EXACT:
+            c = _f16_exact(g * c0)
+            e = [min((X[i][j] - r[i] * c * q for q in range(-qm, qm + 1)), key=abs) for i in range(dk)]
+            F = sum(w[i] * e[i] * e[i] for i in range(dk))
+            if best is None or F < best[0]:
+                best = (F, e)
+        for i in range(dk):
+            err[i][j] = best[1][i] ** 2
+    return err
+
+
+def test_distortion_worked_example_2x2():
+    """Hand-worked 2x2 state, one calibration snapshot, w = (1, 1/4), grid {1, 7/8, 3/4, 5/8}.
+
+    X = [[4, 1], [9/4, -3/4]].  Row factors r = sqrt(m / w): r0 = sqrt(4 / 1) = 2, r1 = sqrt((9/4) / (1/4)) = 3
+    (binary16-exact).  t = X / r = [[2, 1/2], [3/4, -1/4]].
+    Width 2 (qmax 1): c0 = (2, 1/2).
+      column 0, t = (2, 3/4):
+        c = 2:    z = (1, 3/8)   Q = (1, 0)  X^ = (4, 0)       err = (0, 9/4)     F = 81/64
+        c = 7/4:  z = (8/7, 3/7) Q = (1, 0)  X^ = (7/2, 0)     err = (1/2, 9/4)   F = 97/64
+        c = 3/2:  z = (4/3, 1/2) Q = (1, 0)  (the tie rounds to even)  err = (1, 9/4)  F = 145/64
+        c = 5/4:  z = (8/5, 3/5) Q = (1, 1)  X^ = (5/2, 15/4)  err = (3/2, -3/2)  F = 45/16
+        -> c = 2, squared errors (0, 81/16)
+      column 1, t = (1/2, -1/4):
+        c = 1/2:  z = (1, -1/2)    Q = (1, 0)   err = (0, -3/4)      F = 9/64
+        c = 7/16: z = (8/7, -4/7)  Q = (1, -1)  X^ = (7/8, -21/16)  err = (1/8, 9/16)  F = 97/1024
+        c = 3/8:  z = (4/3, -2/3)  Q = (1, -1)  err = (1/4, 3/8)     F = 100/1024
+        c = 5/16: z = (8/5, -4/5)  Q = (1, -1)  err = (3/8, 3/16)    F = 153/1024
+        -> c = 7/16, squared errors (1/64, 81/256)
+      D_row = (1/64, 81/16 + 81/256) = (1/64, 1377/256);  D_head = 1381/256.
+      (Weighting the distortion by w would give D_head = 1/64 + 1377/1024 = 1393/1024.)
+    Width 4 (qmax 7): c0 = (2/7, 1/14); binary16(2/7) = 1170 * 2^-12 = 585/2048, binary16(1/14) = 585/8192,
+      binary16(7/8 * 2/7) = 1/4; both columns keep gamma = 1 (F = 431665/2^24 against 1/4, and
+      23981/2^23 against 1/64), codes [[7, 7], [3, -4]]:
+      column 0 errors (4 - 2 * 7 * 585/2048, 9/4 - 3 * 3 * 585/2048) = (1/1024, -3/2048);
+      D_row = (17/2^24, 239805/2^21), D_head = 1918457/2^24.
+    Widths 6 and 8 (qmax 31, 127): values from the exact brute force below, D_head = 6272657/2^30 and
+      92177/2^28, D_row = (17/2^30, 49005/2^23) and (17/2^28, 45/2^17).
+    """
+    X = np.array([[[4.0, 1.0], [2.25, -0.75]]])
+    w = np.array([1.0, 0.25])
+    expect_head = {2: Fr(1381, 256), 4: Fr(1918457, 2 ** 24), 6: Fr(6272657, 2 ** 30), 8: Fr(92177, 2 ** 28)}
+    expect_row = {2: (Fr(1, 64), Fr(1377, 256)), 4: (Fr(17, 2 ** 24), Fr(239805, 2 ** 21)),
+                  6: (Fr(17, 2 ** 30), Fr(49005, 2 ** 23)), 8: (Fr(17, 2 ** 28), Fr(45, 2 ** 17))}
+    widths = (2, 4, 6, 8)
+    Dh = planner.head_distortion(X, w, widths, GRID4, "head")
+    Dr = planner.head_distortion(X, w, widths, GRID4, "row")
+    for k, b in enumerate(widths):
+        assert Dh[0, k] == pytest.approx(float(expect_head[b]), rel=1e-12), b
+        assert Dr[:, k] == pytest.approx([float(v) for v in expect_row[b]], rel=1e-12, abs=1e-300), b
+    # the exact brute force reproduces the hand-worked values
+    Xf = [[Fr(4), Fr(1)], [Fr(9, 4), Fr(-3, 4)]]
+    for b in widths:
+        e = _exact_state_error(Xf, [Fr(1), Fr(1, 4)], b)
+        assert sum(map(sum, e)) == expect_head[b]
+        assert (sum(e[0]), sum(e[1])) == expect_row[b]
+
+
+def _dyadic_state(seed, n, dk, dv, den=16, span=48):
+    g = np.random.default_rng(seed)
+    return g.integers(-span, span + 1, size=(n, dk, dv)) / den
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_distortion_equals_exact_brute_force_4x4(seed):
+    """Two 4x4 calibration snapshots (dyadic entries, a zero column in one of them), w non-uniform: D_u(b) at
+    widths 2, 4, 6 and 8 for head and row units equals the mean over the snapshots of the exact squared errors
+    of the brute-force quantizer."""
+    S = _dyadic_state(40 + seed, 2, 4, 4)
+    S[1, :, 2] = 0.0
+    w = np.array([1.0, 0.25, 2.0, 0.5625])
+    widths = (2, 4, 6, 8)
+    Dh = planner.head_distortion(S, w, widths, GRID4, "head")
+    Dr = planner.head_distortion(S, w, widths, GRID4, "row")
+    wf = [Fr(x) for x in w.tolist()]
+    for k, b in enumerate(widths):
+        per_row = [Fr(0)] * 4
+        for s in range(2):
+            Xf = [[Fr(x) for x in row] for row in S[s].tolist()]
+            e = _exact_state_error(Xf, wf, b)
+            for i in range(4):
+                per_row[i] += sum(e[i]) / 2
+        assert Dh[0, k] == pytest.approx(float(sum(per_row)), rel=1e-12), b
+        assert Dr[:, k] == pytest.approx([float(v) for v in per_row], rel=1e-12, abs=1e-300), b
+    assert np.all(np.diff(Dh[0]) < 0)
+
+
+def test_calibration_snapshot_three_tokens():
+    """Three tokens from the zero state, beta = 1/2, k = (1, 0), (0, 1), (3/5, 4/5), v = (2, 4), (4, 2), (1, 1).
+
+    GDN, alpha = 1/2:
+      token 1: X = (1/2) k v^T                                      = [[1, 2], [0, 0]]
+      token 2: D X = [[1/2, 1], [0, 0]], k^T D X = (0, 0), e = (4, 2) -> [[1/2, 1], [2, 1]]
+      token 3: D X = [[1/4, 1/2], [1, 1/2]], k^T D X = (0.95, 0.7), e = (0.05, 0.3)
+               X = D X + (1/2) k e^T                                 = [[0.265, 0.59], [1.02, 0.62]]
+    KDA, alpha = (1/2, 1): tokens 1-2 as above (row 1 is still zero after token 1), then
+      token 3: D X = [[1/4, 1/2], [2, 1]], k^T D X = (1.75, 1.1), e = (-0.75, -0.1)
+               X = [[0.025, 0.47], [1.7, 0.96]]
+    (Dropping the last token leaves [[1/2, 1], [2, 1]]; restarting from zero at every token gives
+    (1/2) k3 v3^T = [[0.3, 0.3], [0.4, 0.4]].)"""
+    k = np.array([[[1.0, 0.0], [0.0, 1.0], [0.6, 0.8]]])
+    v = np.array([[[2.0, 4.0], [4.0, 2.0], [1.0, 1.0]]])
+    q = np.ones_like(k)
+    beta = np.full((1, 3), 0.5)
+    gdn = planner.calib_snapshots(q, k, v, beta, 0.5)
+    assert gdn.shape == (1, 2, 2)
+    assert np.allclose(gdn[0], [[0.265, 0.59], [1.02, 0.62]], rtol=0, atol=1e-14)
+    kda = planner.calib_snapshots(q, k, v, beta, np.array([0.5, 1.0]))
+    assert np.allclose(kda[0], [[0.025, 0.47], [1.7, 0.96]], rtol=0, atol=1e-14)
+    # two segments are independent: the second segment's state does not see the first's tokens
+    both = planner.calib_snapshots(np.concatenate([q, q]), np.concatenate([k, k[:, ::-1]]),
+                                   np.concatenate([v, v]), np.concatenate([beta, beta]), 0.5)
+    assert np.allclose(both[0], gdn[0], rtol=0, atol=1e-14)
+    assert not np.allclose(both[1], gdn[0])
