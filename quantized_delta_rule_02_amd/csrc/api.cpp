@@ -360,7 +360,7 @@ extern "C" sq_status sq_pool_create(const sq_plan* p, void* d_pool, size_t pool_
     if (st == SQ_OK) st = upload(pl, p->scale_off, &pl->t.scale_off);
     if (st == SQ_OK) st = upload(pl, p->perm, &pl->t.perm);
     if (st == SQ_OK) st = upload(pl, p->srow_bits, &pl->t.row_bits);
-    if (st == SQ_OK) st = upload(pl, p->srow_w, &pl->t.row_w);
+    if (st == SQ_OK) st = upload(pl, p->srow_wf, reinterpret_cast<const float**>(&pl->t.row_wf));
     if (st == SQ_OK) st = upload(pl, p->head_flags, &pl->t.head_flags);
     if (st != SQ_OK) { sq_pool_destroy(pl); return st; }
     *out = pl;
@@ -383,6 +383,7 @@ static sq_status check_range(const sq_pool* pl, int32_t layer0, int32_t n_layers
         return SQ_ERR_PLAN_MISMATCH;
     }
     if (batch < 0 || batch > pl->n_slots) { set_error("batch %d with %d slots", batch, pl->n_slots); return SQ_ERR_ARG; }
+    if (batch > 65535) { set_error("batch %d above 65535 requests per call", batch); return SQ_ERR_ARG; }
     const int64_t n_states = int64_t(n_layers) * batch * pl->H;
     if (n_states > int64_t(0x7FFFFFFF)) { set_error("too many states in one call"); return SQ_ERR_ARG; }
     return SQ_OK;
@@ -412,6 +413,7 @@ static StepParams base_params(const sq_pool* pl, int32_t layer0, int32_t n_layer
     p.n_layers = n_layers;
     p.batch = batch;
     p.form = pl->form;
+    p.n_slots = pl->n_slots;
     p.slots = slots;
     p.n_grid = pl->n_grid;
     p.quant_mode = pl->quantizer;
@@ -439,10 +441,9 @@ extern "C" sq_status sq_state_step(sq_pool* pl, int32_t layer0, int32_t n_layers
     }
     StepParams p = base_params(pl, layer0, n_layers, batch, d_slots);
     p.q = d_q; p.k = d_k; p.v = d_v; p.gate = d_gate; p.beta = d_beta; p.y = d_y;
-    const int n_states = n_layers * batch * pl->H;
     hipError_t e;
     if (!(flags & SQ_STEP_SPLIT)) {
-        e = launch_state(pl->dk, pl->dv, kModeStep, p, n_states, sm);
+        e = launch_state(pl->dk, pl->dv, kModeStep, p, batch, n_layers, sm);
         return e == hipSuccess ? SQ_OK : hip_fail(e, "state step launch");
     }
     // split arrangement: per chunk, readout kernel on the main stream, fit + pack on the aux stream.
@@ -459,9 +460,10 @@ extern "C" sq_status sq_state_step(sq_pool* pl, int32_t layer0, int32_t n_layers
     }
     p.e_buf = pl->e_buf + size_t(layer0) * size_t(layer_stride) * pl->dv;
     p.e_layer_stride = layer_stride;
+    // chunks: one layer each, or for a single layer up to four ranges of requests
     const int per_layer = batch * pl->H;
     const int n_chunks = n_layers > 1 ? n_layers : std::min(4, std::max(1, per_layer / 256));
-    const int chunk = (n_states + n_chunks - 1) / n_chunks;
+    const int chunk_b = n_layers > 1 ? batch : (batch + n_chunks - 1) / n_chunks;
     while (int(pl->events.size()) < 2 * n_chunks + 1) {
         hipEvent_t ev;
         e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
@@ -475,18 +477,18 @@ extern "C" sq_status sq_state_step(sq_pool* pl, int32_t layer0, int32_t n_layers
         if (e != hipSuccess) return hip_fail(e, "ordering the aux stream");
     }
     for (int c = 0; c < n_chunks; ++c) {
-        const int s0 = c * chunk;
-        const int ns = std::min(chunk, n_states - s0);
-        if (ns <= 0) break;
-        p.state0 = s0;
-        e = launch_state(pl->dk, pl->dv, kModeSplitA, p, ns, sm);
+        p.lz0 = n_layers > 1 ? c : 0;
+        p.b0 = n_layers > 1 ? 0 : c * chunk_b;
+        const int nb = std::min(chunk_b, batch - p.b0);
+        if (nb <= 0) break;
+        e = launch_state(pl->dk, pl->dv, kModeSplitA, p, nb, 1, sm);
         if (e != hipSuccess) return hip_fail(e, "split readout launch");
         if (sa != sm) {
             e = hipEventRecord(pl->events[2 * c], sm);
             if (e == hipSuccess) e = hipStreamWaitEvent(sa, pl->events[2 * c], 0);
             if (e != hipSuccess) return hip_fail(e, "split event");
         }
-        e = launch_state(pl->dk, pl->dv, kModeSplitB, p, ns, sa);
+        e = launch_state(pl->dk, pl->dv, kModeSplitB, p, nb, 1, sa);
         if (e != hipSuccess) return hip_fail(e, "split fit/pack launch");
     }
     if (sa != sm && !(flags & SQ_STEP_NO_JOIN)) {
@@ -507,7 +509,7 @@ extern "C" sq_status sq_pack(sq_pool* pl, int32_t layer0, int32_t n_layers, int3
     if (!d_slots || !d_X) { set_error("NULL device array"); return SQ_ERR_ARG; }
     StepParams p = base_params(pl, layer0, n_layers, batch, d_slots);
     p.x_in = d_X;
-    hipError_t e = launch_state(pl->dk, pl->dv, kModePack, p, n_layers * batch * pl->H, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_state(pl->dk, pl->dv, kModePack, p, batch, n_layers, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SQ_OK : hip_fail(e, "pack launch");
 }
 
@@ -519,7 +521,7 @@ extern "C" sq_status sq_unpack(sq_pool* pl, int32_t layer0, int32_t n_layers, in
     if (!d_slots || !d_X) { set_error("NULL device array"); return SQ_ERR_ARG; }
     StepParams p = base_params(pl, layer0, n_layers, batch, d_slots);
     p.x_out = d_X;
-    hipError_t e = launch_state(pl->dk, pl->dv, kModeUnpack, p, n_layers * batch * pl->H, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_state(pl->dk, pl->dv, kModeUnpack, p, batch, n_layers, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SQ_OK : hip_fail(e, "unpack launch");
 }
 
@@ -531,7 +533,7 @@ static sq_status codec(sq_pool* pl, bool do_export, int32_t layer0, int32_t n_la
     if (!d_slots || !codes || !r || !c) { set_error("NULL device array"); return SQ_ERR_ARG; }
     CodecParams p{};
     p.pool = pl->pool; p.slot_bytes = pl->slot_bytes; p.t = pl->t; p.n_heads = pl->H; p.layer0 = layer0;
-    p.batch = batch; p.slots = d_slots; p.codes = codes; p.r = r; p.c = c;
+    p.batch = batch; p.n_slots = pl->n_slots; p.slots = d_slots; p.codes = codes; p.r = r; p.c = c;
     hipError_t e = launch_codec(pl->dk, pl->dv, do_export, p, n_layers * batch * pl->H, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SQ_OK : hip_fail(e, do_export ? "export launch" : "import launch");
 }

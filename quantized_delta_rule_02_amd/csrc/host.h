@@ -22,7 +22,7 @@ struct sq_plan {
     // layout (see internal.h)
     std::vector<uint16_t> perm;                      // [LH][dk]
     std::vector<uint8_t> srow_bits;                  // [LH][dk]
-    std::vector<float> srow_w;                       // [LH][dk]
+    std::vector<float> srow_wf;                      // [LH][dk][2]: 1 / w and sqrt(w) of each storage row
     std::vector<uint8_t> grp_bits;                   // [LH][NG]
     std::vector<uint32_t> grp_off;                   // [LH][NG]
     std::vector<uint32_t> scale_off;                 // [LH]

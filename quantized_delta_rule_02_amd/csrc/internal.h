@@ -30,6 +30,7 @@
 //   groups per head use a wider container than their rows need.
 #pragma once
 #include <stdint.h>
+#include <hip/hip_vector_types.h>
 
 namespace sq {
 
@@ -58,7 +59,7 @@ struct DevTables {
     const uint32_t* scale_off;  // [LH] byte offset of the binary16 row factors (column scales follow)
     const uint16_t* perm;       // [LH][d_k] storage row -> canonical row
     const uint8_t* row_bits;    // [LH][d_k] code width of the row, 16 = pivot (storage order)
-    const float* row_w;         // [LH][d_k] row-impact score (storage order)
+    const float2* row_wf;       // [LH][d_k] 1 / w and sqrt(w) of the row-impact score w (storage order)
     const uint8_t* head_flags;  // [LH]
 };
 
@@ -69,6 +70,7 @@ struct StepParams {
     uint64_t slot_bytes;
     DevTables t;
     int32_t n_heads, layer0, n_layers, batch, form;
+    int32_t n_slots;     // slots of the pool: a request whose slot is outside [0, n_slots) is skipped
     const int32_t* slots;
     const float* q;
     const float* k;
@@ -80,7 +82,8 @@ struct StepParams {
     float* x_out;        // unpack: float states
     float* e_buf;        // split arrangement: v - k^T D S, [layer][request index][head][d_v] from layer0
     int64_t e_layer_stride;  // split arrangement: states per layer of e_buf (n_slots * n_heads)
-    int32_t state0;      // split arrangement: first state of the chunk
+    int32_t lz0;         // first layer of the launch, relative to layer0 (split arrangement: of the chunk)
+    int32_t b0;          // first request of the launch
     int32_t n_grid;
     int32_t unit_first;  // grid[0] == 1: the first candidate needs no clamp
     int32_t quant_mode;  // SQ_QUANT_DUAL_AXIS or SQ_QUANT_ROW_ABSMAX
@@ -93,6 +96,7 @@ struct CodecParams {
     uint64_t slot_bytes;
     DevTables t;
     int32_t n_heads, layer0, batch;
+    int32_t n_slots;     // a request whose slot is outside [0, n_slots) is skipped
     const int32_t* slots;
     int16_t* codes;      // canonical [state][d_k][d_v]
     uint16_t* r;         // [state][d_k]

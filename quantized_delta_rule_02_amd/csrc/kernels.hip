@@ -57,6 +57,14 @@ __device__ __forceinline__ int bias_of(int bits) { return bits == 16 ? 0 : (1 <<
 // query functions are built with IEEE mode on, so with IEEE mode off here they are not inlined:
 // each kernel would call them and receive the block index in a vector register.
 __device__ __forceinline__ int block_idx() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int block_idy() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+__device__ __forceinline__ int block_idz() { return (int)__builtin_amdgcn_workgroup_id_z(); }
+// A load whose address is the same for every lane, of memory no kernel of the launch writes (plan tables,
+// slot lists, per-state inputs): read through the constant address space, so it becomes a scalar load.
+template <class T>
+__device__ __forceinline__ T ld_const(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)(uintptr_t)p;
+}
 __device__ __forceinline__ int thread_idx() { return (int)__builtin_amdgcn_workitem_id_x(); }
 // a value every lane of the wave holds, moved to a scalar register
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -281,17 +289,18 @@ struct Shape {
 
 template <int DK, int DV>
 struct StepSmem {
-    float4 acc[DK];    // column accumulation: A k, A q (code rows), alpha k, alpha q (pivot rows)
-    float4 upd[DK];    // update: A = alpha r_old (code rows), beta k, alpha (pivot rows), unused
-    float4 fit[DK];    // requantization: 1 / r_new, sqrt(w) r_new, -sqrt(w) r_new / 2, 1/2 - qmax
+    float2 acc[DK];    // column-sum coefficients: D_i r_i (k_i, q_i) on code rows, D_i (k_i, q_i) on pivot rows
+    float2 upd[DK];    // update: D_i r_i (D_i on pivot rows), beta k_i
+    float4 fit[DK];    // requantization: sqrt(w) r_new, -sqrt(w) r_new / 2, 1/2 - qmax, 1 / r_new
     float iq[DK];      // 1 / qmax (0 on pivot rows)
     float2 fin[DK];    // final rounding bounds: magic + container bias -/+ qmax
     float rn[DK];      // new binary16 row factor
-    float w[DK];
+    float2 wf[DK];     // 1 / w and sqrt(w)
     int rb[DK];        // code width of the row (16 = pivot)
-    float part[Shape<DK, DV>::NW][4][DV];   // column sums of k^T D S, q^T D S; later the fit objective
-    float cmax[Shape<DK, DV>::NW][DV];      // column base partial maxima
-    float red[Shape<DK, DV>::NW][4];
+    float stage[Shape<DK, DV>::NW][3][DK];   // each wave's copy of k, q and the per-row gate, canonical order
+    float part[Shape<DK, DV>::NW][4][DV];    // column sums of k^T D S, q^T D S; later the fit objective
+    float cmax[Shape<DK, DV>::NW][DV];       // column base partial maxima
+    float red[Shape<DK, DV>::NW];            // k^T q partials
 };
 
 constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23: x + kMagic rounds x to an integer in the low mantissa bits
@@ -416,11 +425,10 @@ __device__ __forceinline__ void load_group(const uint8_t* gp, int lane, bool act
     }
 }
 
-// Row of the split arrangement's scratch for state sid of a call: (layer - layer0, request, head)
-// with a layer stride of n_slots * n_heads.
-__device__ __forceinline__ size_t e_index(const StepParams& a, int sid) {
-    const int per_layer = a.n_heads * a.batch;
-    return (size_t)(sid / per_layer) * (size_t)a.e_layer_stride + (size_t)(sid % per_layer);
+// Row of the split arrangement's scratch for (layer lz of the call, request b, head h), with a layer
+// stride of n_slots * n_heads.
+__device__ __forceinline__ size_t e_index(const StepParams& a, int lz, int b, int h) {
+    return (size_t)lz * (size_t)a.e_layer_stride + (size_t)b * a.n_heads + h;
 }
 
 // Stored codes carry the container's offset 2^(W-1).  One FMA per entry turns a stored code into
@@ -450,7 +458,7 @@ __device__ __forceinline__ void unpack_acc_uniform(uint32_t (&raw)[Sh::GPW][4], 
         else if constexpr (W == 8) unpack8(raw[g], xg);
         else if constexpr (W == 2) unpack2f(raw[g][0], xg);
         else {
-            const uint32_t hi = act ? *reinterpret_cast<const uint16_t*>(rec + uniform(goff[wave * GPW + g]) +
+            const uint32_t hi = act ? *reinterpret_cast<const uint16_t*>(rec + ld_const(goff + wave * GPW + g) +
                                                                        LPR * 4 + lane * 2) : 0u;
             unpack3f(raw[g][0], hi, xg);
         }
@@ -458,7 +466,7 @@ __device__ __forceinline__ void unpack_acc_uniform(uint32_t (&raw)[Sh::GPW][4], 
         if constexpr (ACC) {
 #pragma unroll
             for (int r = 0; r < GR; ++r) {
-                const float2 cf = *reinterpret_cast<const float2*>(&sm.acc[wave * RPW + g * GR + r]);
+                const float2 cf = sm.acc[wave * RPW + g * GR + r];
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     U1[c] = fmaf(cf.x, xg[r * CPL + c], U1[c]);
@@ -474,9 +482,12 @@ template <bool ACC, class Sh, class Smem>
 __device__ __forceinline__ void acc_group(const Smem& sm, int wave, int g, const float* xg, float* U1, float* P1) {
     constexpr int CPL = Sh::CPL, GR = Sh::GR, RPW = Sh::RPW;
     if constexpr (ACC) {
+        // called inside each width branch: the memory clobber keeps the group's coefficient reads inside the
+        // branch (hoisted above the width dispatch, they are held across the unpack and spill)
+        __asm__ volatile("" ::: "memory");
 #pragma unroll
         for (int r = 0; r < GR; ++r) {
-            const float2 cf = *reinterpret_cast<const float2*>(&sm.acc[wave * RPW + g * GR + r]);
+            const float2 cf = sm.acc[wave * RPW + g * GR + r];
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 U1[c] = fmaf(cf.x, xg[r * CPL + c], U1[c]);
@@ -494,7 +505,7 @@ __device__ __forceinline__ void round_pack_uniform(const float* X, const float* 
     const float mb = kMagic + (float)bias_of(W);
 #pragma unroll
     for (int g = 0; g < GPW; ++g) {
-        uint8_t* gp = rec + uniform(goff[wave * GPW + g]);
+        uint8_t* gp = rec + ld_const(goff + wave * GPW + g);
         float m[16];
         uint32_t d[4];
 #pragma unroll
@@ -539,7 +550,7 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
     float cg[KG][CPL], icg[KG][CPL], Fp[KG][CPL];
     // the rows' LDS addresses are formed inside each round: hoisted out of the caller's round loop
     // they would hold RPW registers across it
-    int rbase = wave * RPW;
+    int rbase = uniform(wave * RPW);
     if constexpr (!FREE0) __asm__ volatile("" : "+s"(rbase));
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
@@ -562,7 +573,7 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
                 for (int c = 0; c < CPL; ++c) __asm__ volatile("" : "+v"(icg[j][c]));
         }
         const float4 f = sm.fit[rbase + r];
-        const float sw = f.y, nsw = f.z, hq = f.w;
+        const float sw = f.x, nsw = f.y, hq = f.z;
         // The error is odd in t and round-half-even is symmetric, so the fit works on |t| (a free
         // source modifier).  The first candidate of a round that starts at gamma = 1 cannot clip (the
         // caller checks that no column base exceeds the binary16 range) and skips the max.  The row's KG x CPL chains advance in stages separated by empty asm
@@ -636,33 +647,64 @@ k_state(StepParams a) {
     constexpr bool kAccum = (MODE == kModeStep || MODE == kModeSplitA);
     __shared__ StepSmem<DK, DV> sm;
 
-    const int sid = block_idx() + a.state0;
-    const int h = sid % a.n_heads;
-    const int b = (sid / a.n_heads) % a.batch;
-    const int l = a.layer0 + sid / (a.n_heads * a.batch);
-    const int lh = l * a.n_heads + h;
-    // per-state table values are the same for every lane: keep them in scalar registers so that
-    // the width dispatch below is a uniform branch
-    const int slot = uniform(a.slots[b]);
-    uint8_t* rec = a.pool + (uint64_t)slot * a.slot_bytes + uniform64(a.t.rec_off[lh]);
-    uint16_t* rs = reinterpret_cast<uint16_t*>(rec + uniform(a.t.scale_off[lh]));   // row factors, then column scales
+    // workgroup (x, y, z) = (head, request - b0, layer - layer0 - lz0): no index division
+    const int h = block_idx();
+    const int b = a.b0 + block_idy();
+    const int lz = a.lz0 + block_idz();
+    const int sid = (lz * a.batch + b) * a.n_heads + h;   // index of the state in the call's input arrays
+    const int lh = (a.layer0 + lz) * a.n_heads + h;
+    // per-state table values are the same for every lane: scalar loads, kept in scalar registers so
+    // that the width dispatch below is a uniform branch
+    const int slot = ld_const(a.slots + b);
+    // a slot outside [0, n_slots) skips the state (uniform over the workgroup, before any barrier)
+    if ((unsigned)slot >= (unsigned)a.n_slots) return;
+    uint8_t* rec = a.pool + (uint64_t)slot * a.slot_bytes + ld_const(a.t.rec_off + lh);
+    uint16_t* rs = reinterpret_cast<uint16_t*>(rec + ld_const(a.t.scale_off + lh));   // row factors, then column scales
     const int tid = thread_idx(), wave = uniform(tid >> 6), lane = tid & 63;
     const bool act = lane < LPR;
     const int col0 = lane * CPL;
     const uint8_t* gbits = a.t.grp_bits + (size_t)lh * NG;
     const uint32_t* goff = a.t.grp_off + (size_t)lh * NG;
-    const int hflags = uniform(a.t.head_flags[lh]);
+    const int hflags = uniform((int)a.t.head_flags[lh]);   // a byte: no scalar load, a vector load + readfirstlane
 
-    // ---- issue the loads of this wave's packed groups first; they overlap phase 0.  Every lane
-    // loads 4 dwords at its stride 2b bytes: a 4- or 6-bit lane over-reads into its neighbour's
-    // data (or the record's scale vectors after the last group), a 16-bit lane gets its first half.
+    // ---- every load of the state is issued here, at most one dependent level deep (the slot, then the
+    // record): the packed groups and scales of the record; the plan's tables; the step's inputs, with
+    // k, q and the per-row gate read in canonical order (not through the row permutation, which would
+    // add a level) and staged through LDS.  Every lane loads 4 dwords of each group at its stride 2b
+    // bytes: a 4- or 6-bit lane over-reads into its neighbour's data (or the record's scale vectors after
+    // the last group), a 16-bit lane gets its first half.
+    constexpr int EK = DK >= 64 ? DK / 64 : 1;   // canonical k / q / gate entries per lane
+    float kc[EK], qc[EK], gc[EK], vv[CPL];
+    if constexpr (kUpdate) {
+        if (lane * EK < DK) {
+#pragma unroll
+            for (int e = 0; e < EK; ++e) {
+                kc[e] = a.k[(size_t)sid * DK + lane * EK + e];
+                qc[e] = a.q[(size_t)sid * DK + lane * EK + e];
+                gc[e] = (a.form == 1) ? a.gate[(size_t)sid * DK + lane * EK + e] : 1.f;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            if constexpr (MODE == kModeSplitB) vv[c] = act ? a.e_buf[e_index(a, lz, b, h) * DV + col0 + c] : 0.f;
+            else vv[c] = act ? a.v[(size_t)sid * DV + col0 + c] : 0.f;
+        }
+    }
     uint32_t raw[GPW][4];
     int gb[GPW];
+    if constexpr (GPW == 4 && NG % 4 == 0) {
+        // the wave's four container widths are one aligned dword of the table: one scalar load
+        const uint32_t w4 = ld_const(reinterpret_cast<const uint32_t*>(gbits + wave * GPW));
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) gb[g] = (int)((w4 >> (8 * g)) & 0xFFu);
+    } else {
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) gb[g] = uniform((int)gbits[wave * GPW + g]);
+    }
 #pragma unroll
     for (int g = 0; g < GPW; ++g) {
-        gb[g] = uniform(gbits[wave * GPW + g]);
         if constexpr (MODE != kModePack) {
-            const uint8_t* gp = rec + uniform(goff[wave * GPW + g]);
+            const uint8_t* gp = rec + ld_const(goff + wave * GPW + g);
             // one unconditional load per group (a branch here would make the compiler wait for it);
             // a 3-bit lane's dword sits at stride 4, its third-bit plane is loaded in phase 1
             if (act) load_dw<4>(gp + lane * ((NARROW && gb[g] == 3) ? 4 : 2 * gb[g]), raw[g]);
@@ -677,34 +719,53 @@ k_state(StepParams a) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) c_old[c] = act ? h2f(rs[DK + col0 + c]) : 1.f;
     }
+    int rbits = 16, perm = 0;
+    float2 wrow = make_float2(1.f, 1.f);
+    float rold = 1.f;
+    if (lane < RPW) {
+        const size_t t = (size_t)lh * DK + wave * RPW + lane;
+        rbits = a.t.row_bits[t];
+        wrow = a.t.row_wf[t];
+        perm = a.t.perm[t];
+        if constexpr (kNeedOld) rold = h2f(rs[wave * RPW + lane]);
+    }
 
     // ---- phase 0: per-row coefficients of this wave's rows (lane r < RPW takes row wave * RPW + r)
+    if constexpr (kUpdate) {
+        if (lane * EK < DK) {
+#pragma unroll
+            for (int e = 0; e < EK; ++e) {
+                sm.stage[wave][0][lane * EK + e] = kc[e];
+                sm.stage[wave][1][lane * EK + e] = qc[e];
+                sm.stage[wave][2][lane * EK + e] = gc[e];
+            }
+        }
+        wave_lds_sync();
+    }
     float kq_part = 0.f;
     if (lane < RPW) {
         const int t = wave * RPW + lane;
-        const int rbits = a.t.row_bits[(size_t)lh * DK + t];
         const bool piv = rbits == 16;
         sm.rb[t] = rbits;
-        sm.w[t] = a.t.row_w[(size_t)lh * DK + t];
+        sm.wf[t] = wrow;
         if constexpr (kNeedOld) {
-            const float rold = h2f(rs[t]);
             float al = 1.f, kk = 0.f, qq = 0.f, bt = 0.f;
             if constexpr (kUpdate) {
-                const int i = a.t.perm[(size_t)lh * DK + t];
-                kk = a.k[(size_t)sid * DK + i];
-                qq = a.q[(size_t)sid * DK + i];
-                al = (a.form == 1) ? a.gate[(size_t)sid * DK + i] : a.gate[sid];
-                bt = a.beta[sid];
+                kk = sm.stage[wave][0][perm];
+                qq = sm.stage[wave][1][perm];
+                al = (a.form == 1) ? sm.stage[wave][2][perm] : ld_const(a.gate + sid);
+                bt = ld_const(a.beta + sid);
             }
-            const float A = piv ? 0.f : al * rold;
-            sm.acc[t] = make_float4(A * kk, A * qq, piv ? al * kk : 0.f, piv ? al * qq : 0.f);
-            sm.upd[t] = make_float4(A, bt * kk, piv ? al : 0.f, 0.f);
+            // a pivot row stores its value as is: its coefficient is the gate alone
+            const float A = piv ? al : al * rold;
+            sm.acc[t] = make_float2(A * kk, A * qq);
+            sm.upd[t] = make_float2(A, bt * kk);
             kq_part = kk * qq;
         }
     }
     if constexpr (kAccum) {
         kq_part = wave_sum(kq_part);
-        if (lane == 0) sm.red[wave][0] = kq_part;
+        if (lane == 0) sm.red[wave] = kq_part;
     }
     wave_lds_sync();
 
@@ -719,9 +780,9 @@ k_state(StepParams a) {
             X[e] = act ? a.x_in[((size_t)sid * DK + i) * DV + col0 + (e % CPL)] : 0.f;
         }
     } else {
-        float U1[CPL], P1[CPL], U2[CPL], P2[CPL];
+        float U1[CPL], P1[CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) U1[c] = P1[c] = U2[c] = P2[c] = 0.f;
+        for (int c = 0; c < CPL; ++c) U1[c] = P1[c] = 0.f;
         bool same = true;
 #pragma unroll
         for (int g = 1; g < GPW; ++g) same = same && gb[g] == gb[0];
@@ -749,7 +810,7 @@ k_state(StepParams a) {
                 acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1);
             }
             else if (NARROW && gb[g] == 3) {
-                const uint32_t hi = act ? *reinterpret_cast<const uint16_t*>(rec + uniform(goff[wave * GPW + g]) +
+                const uint32_t hi = act ? *reinterpret_cast<const uint16_t*>(rec + ld_const(goff + wave * GPW + g) +
                                                                            LPR * 4 + lane * 2) : 0u;
                 unpack3f(raw[g][0], hi, xg);
                 scale_codes<CPL>(xg, c_old, 4.f);
@@ -769,7 +830,7 @@ k_state(StepParams a) {
                 uint32_t d16[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) d16[i] = raw[g][i];
-                if (act) load_dw<4>(rec + uniform(goff[wave * GPW + g]) + lane * 32 + 16, d16 + 4);
+                if (act) load_dw<4>(rec + ld_const(goff + wave * GPW + g) + lane * 32 + 16, d16 + 4);
                 else d16[4] = d16[5] = d16[6] = d16[7] = 0;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -778,17 +839,6 @@ k_state(StepParams a) {
                     xg[e] = (sm.rb[t] == 16) ? h2f(bits) : c_old[e % CPL] * (float)(int16_t)bits;
                 }
                 acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1);
-                if constexpr (kAccum) {
-#pragma unroll
-                    for (int r = 0; r < GR; ++r) {
-                        const float4 cf = sm.acc[wave * RPW + g * GR + r];
-#pragma unroll
-                        for (int c = 0; c < CPL; ++c) {
-                            U2[c] = fmaf(cf.z, xg[r * CPL + c], U2[c]);
-                            P2[c] = fmaf(cf.w, xg[r * CPL + c], P2[c]);
-                        }
-                    }
-                }
             }
         }
 
@@ -798,9 +848,7 @@ k_state(StepParams a) {
             for (int e = 0; e < EPL; ++e) {
                 const int t = wave * RPW + e / CPL;
                 const int c = e % CPL;
-                const float4 u = sm.upd[t];
-                const bool piv = sm.rb[t] == 16;
-                const float s = piv ? X[e] : u.x * X[e];
+                const float s = sm.upd[t].x * X[e];   // r_i c_j Q_ij (1 times the value on pivot rows)
                 const int i = a.t.perm[(size_t)lh * DK + t];
                 if (act) a.x_out[((size_t)sid * DK + i) * DV + col0 + c] = s;
             }
@@ -814,70 +862,44 @@ k_state(StepParams a) {
                 for (int c = 0; c < CPL; ++c) {
                     sm.part[wave][0][col0 + c] = U1[c];
                     sm.part[wave][1][col0 + c] = P1[c];
-                    sm.part[wave][2][col0 + c] = U2[c];
-                    sm.part[wave][3][col0 + c] = P2[c];
                 }
             }
             __syncthreads();
             float kq = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) kq += sm.red[w][0];
-            const float bt = a.beta[sid];
+            for (int w = 0; w < NW; ++w) kq += sm.red[w];
+            const float bt = ld_const(a.beta + sid);
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                float su = 0.f, sp = 0.f, su2 = 0.f, sp2 = 0.f;
+                float su = 0.f, sp = 0.f;
                 if (act) {
 #pragma unroll
                     for (int w = 0; w < NW; ++w) {
                         su += sm.part[w][0][col0 + c];
                         sp += sm.part[w][1][col0 + c];
-                        su2 += sm.part[w][2][col0 + c];
-                        sp2 += sm.part[w][3][col0 + c];
                     }
                 }
-                const float u = su + su2;      // k^T D S
-                const float p = sp + sp2;      // q^T D S
-                const float e = act ? a.v[(size_t)sid * DV + col0 + c] - u : 0.f;
+                // su = k^T D S, sp = q^T D S
+                const float e = act ? vv[c] - su : 0.f;
                 ecol[c] = e;
-                if (act && wave == 0) a.y[(size_t)sid * DV + col0 + c] = fmaf(bt * kq, e, p);
+                if (act && wave == 0) a.y[(size_t)sid * DV + col0 + c] = fmaf(bt * kq, e, sp);
                 if constexpr (MODE == kModeSplitA) {
-                    if (act && wave == 0) a.e_buf[e_index(a, sid) * DV + col0 + c] = e;
+                    if (act && wave == 0) a.e_buf[e_index(a, lz, b, h) * DV + col0 + c] = e;
                 }
             }
             if constexpr (MODE == kModeSplitA) return;
         } else {
             // split arrangement, second half: e = v - k^T D S comes from the first kernel
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) ecol[c] = act ? a.e_buf[e_index(a, sid) * DV + col0 + c] : 0.f;
+            for (int c = 0; c < CPL; ++c) ecol[c] = vv[c];
         }
 
         // ---- phase 2: the updated float state X = D S + beta k e^T in registers
 #pragma unroll
-        for (int g = 0; g < GPW; ++g) {
-            if (gb[g] != 16) {
+        for (int r = 0; r < RPW; ++r) {
+            const float2 u = sm.upd[wave * RPW + r];
 #pragma unroll
-                for (int r = 0; r < GR; ++r) {
-                    const float4 u = sm.upd[wave * RPW + g * GR + r];
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) {
-                        const int e = 16 * g + r * CPL + c;
-                        X[e] = fmaf(u.x, X[e], u.y * ecol[c]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < GR; ++r) {
-                    const int t = wave * RPW + g * GR + r;
-                    const float4 u = sm.upd[t];
-                    const bool piv = sm.rb[t] == 16;
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) {
-                        const int e = 16 * g + r * CPL + c;
-                        const float dq = (piv ? u.z : u.x) * X[e];
-                        X[e] = fmaf(u.y, ecol[c], dq);
-                    }
-                }
-            }
+            for (int c = 0; c < CPL; ++c) X[r * CPL + c] = fmaf(u.x, X[r * CPL + c], u.y * ecol[c]);
         }
     }
 
@@ -898,16 +920,23 @@ k_state(StepParams a) {
             const int rbits = sm.rb[t];
             const bool piv = rbits == 16;
             const float m = rm[0];
-            const float w = sm.w[t];
+            const float2 wf = sm.wf[t];
             const float qmax = piv ? 0.f : (float)((1 << (rbits - 1)) - 1);
             float rn = 1.f;
-            if (!piv && m > 0.f)   // dual-axis sqrt(m / w); the ablation's per-row absmax m / qmax
-                rn = scale_fp16(a.quant_mode == 0 ? __builtin_sqrtf(m * __builtin_amdgcn_rcpf(w)) : m / qmax);
+            // dual-axis sqrt(m / w); the ablation's per-row absmax m / qmax.  The hardware square root and
+            // reciprocal are within a few float32 ulps, far inside the binary16 rounding they feed.
+            if (!piv && m > 0.f)
+                rn = scale_fp16(a.quant_mode == 0 ? __builtin_amdgcn_sqrtf(m * wf.x)
+                                                  : m * __builtin_amdgcn_rcpf(qmax));
             sm.rn[t] = rn;
-            const float sw = piv ? 0.f : __builtin_sqrtf(w) * rn;
-            sm.fit[t] = make_float4(__builtin_amdgcn_rcpf(rn), sw, -0.5f * sw, 0.5f - qmax);
+            const float sw = piv ? 0.f : wf.y * rn;
+            sm.fit[t] = make_float4(sw, -0.5f * sw, 0.5f - qmax, __builtin_amdgcn_rcpf(rn));
             sm.iq[t] = piv ? 0.f : __builtin_amdgcn_rcpf(qmax);
-            const float mb = kMagic + (float)bias_of(gbits[t / GR]);
+            // the row's container width: its group's (wave-uniform values, selected per lane)
+            int cb = gb[0];
+#pragma unroll
+            for (int g = 1; g < GPW; ++g) cb = row >= g * GR ? gb[g] : cb;
+            const float mb = kMagic + (float)bias_of(cb);
             sm.fin[t] = make_float2(mb - qmax, mb + qmax);
         }
     }
@@ -921,7 +950,7 @@ k_state(StepParams a) {
         for (int c = 0; c < CPL; ++c) c0p[c] = 0.f;
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-            const float ir = sm.fit[wave * RPW + r].x;
+            const float ir = sm.fit[wave * RPW + r].w;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) X[r * CPL + c] *= ir;
         }
@@ -1005,7 +1034,7 @@ k_state(StepParams a) {
     for (int g = 0; g < GPW; ++g) {
         const int gg = wave * GPW + g;
         const int sb = gb[g];
-        uint8_t* gp = rec + uniform(goff[gg]);
+        uint8_t* gp = rec + ld_const(goff + gg);
         uint32_t d[8];
         float m[16];
         const float mb = kMagic + (float)bias_of(sb);
@@ -1061,7 +1090,9 @@ k_codec(CodecParams a) {
     const int b = (sid / a.n_heads) % a.batch;
     const int l = a.layer0 + sid / (a.n_heads * a.batch);
     const int lh = l * a.n_heads + h;
-    uint8_t* rec = a.pool + (uint64_t)a.slots[b] * a.slot_bytes + a.t.rec_off[lh];
+    const int slot = a.slots[b];
+    if ((unsigned)slot >= (unsigned)a.n_slots) return;   // uniform over the workgroup: the state is skipped
+    uint8_t* rec = a.pool + (uint64_t)slot * a.slot_bytes + a.t.rec_off[lh];
     uint16_t* rs = reinterpret_cast<uint16_t*>(rec + a.t.scale_off[lh]);
     const int tid = thread_idx(), wave = tid >> 6, lane = tid & 63;
     const int col0 = lane * CPL;
@@ -1196,7 +1227,9 @@ k_cmp(CmpParams a) {
     const int h = sid % a.n_heads;
     const int b = (sid / a.n_heads) % a.batch;
     const int ll = sid / (a.n_heads * a.batch);
-    const size_t st = ((size_t)(a.layer0 + ll) * a.n_slots + a.slots[b]) * a.n_heads + h;
+    const int slot = a.slots[b];
+    if ((unsigned)slot >= (unsigned)a.n_slots) return;   // uniform over the workgroup, before any barrier
+    const size_t st = ((size_t)(a.layer0 + ll) * a.n_slots + slot) * a.n_heads + h;
     const int tid = thread_idx(), wave = tid >> 6, lane = tid & 63;
     const bool act = lane < LPR;
     const int col0 = lane * CPL;
@@ -1350,33 +1383,33 @@ k_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
 // ---------------------------------------------------------------- launchers
 
 template <int DK, int DV, int KG, bool NARROW>
-static hipError_t launch_state_kgn(int mode, const StepParams& p, int n_states, hipStream_t s) {
+static hipError_t launch_state_kgn(int mode, const StepParams& p, dim3 grid, hipStream_t s) {
     const dim3 blk(Shape<DK, DV>::NW * 64);
     switch (mode) {
-        case kModeStep: k_state<DK, DV, kModeStep, KG, NARROW><<<n_states, blk, 0, s>>>(p); break;
-        case kModePack: k_state<DK, DV, kModePack, KG, NARROW><<<n_states, blk, 0, s>>>(p); break;
-        case kModeUnpack: k_state<DK, DV, kModeUnpack, 1, NARROW><<<n_states, blk, 0, s>>>(p); break;
-        case kModeSplitA: k_state<DK, DV, kModeSplitA, 1, NARROW><<<n_states, blk, 0, s>>>(p); break;
-        case kModeSplitB: k_state<DK, DV, kModeSplitB, KG, NARROW><<<n_states, blk, 0, s>>>(p); break;
+        case kModeStep: k_state<DK, DV, kModeStep, KG, NARROW><<<grid, blk, 0, s>>>(p); break;
+        case kModePack: k_state<DK, DV, kModePack, KG, NARROW><<<grid, blk, 0, s>>>(p); break;
+        case kModeUnpack: k_state<DK, DV, kModeUnpack, 1, NARROW><<<grid, blk, 0, s>>>(p); break;
+        case kModeSplitA: k_state<DK, DV, kModeSplitA, 1, NARROW><<<grid, blk, 0, s>>>(p); break;
+        case kModeSplitB: k_state<DK, DV, kModeSplitB, KG, NARROW><<<grid, blk, 0, s>>>(p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 template <int DK, int DV, int KG>
-static hipError_t launch_state_kg(int mode, const StepParams& p, int n_states, hipStream_t s) {
-    return p.narrow ? launch_state_kgn<DK, DV, KG, true>(mode, p, n_states, s)
-                    : launch_state_kgn<DK, DV, KG, false>(mode, p, n_states, s);
+static hipError_t launch_state_kg(int mode, const StepParams& p, dim3 grid, hipStream_t s) {
+    return p.narrow ? launch_state_kgn<DK, DV, KG, true>(mode, p, grid, s)
+                    : launch_state_kgn<DK, DV, KG, false>(mode, p, grid, s);
 }
 
 // candidates per LDS round: one or two when the grid is that small, otherwise four; two for
 // four columns per lane (d_v = 256), where four would spill (a last round with fewer candidates
 // repeats the final one, which cannot change the choice)
 template <int DK, int DV>
-static hipError_t launch_state_t(int mode, const StepParams& p, int n_states, hipStream_t s) {
-    if (p.n_grid == 1) return launch_state_kg<DK, DV, 1>(mode, p, n_states, s);
-    if (p.n_grid == 2 || Shape<DK, DV>::CPL > 2) return launch_state_kg<DK, DV, 2>(mode, p, n_states, s);
-    return launch_state_kg<DK, DV, 4>(mode, p, n_states, s);
+static hipError_t launch_state_t(int mode, const StepParams& p, dim3 grid, hipStream_t s) {
+    if (p.n_grid == 1) return launch_state_kg<DK, DV, 1>(mode, p, grid, s);
+    if (p.n_grid == 2 || Shape<DK, DV>::CPL > 2) return launch_state_kg<DK, DV, 2>(mode, p, grid, s);
+    return launch_state_kg<DK, DV, 4>(mode, p, grid, s);
 }
 
 #define SQ_SHAPES(X) X(16, 16) X(64, 64) X(128, 128) X(128, 256)
@@ -1396,9 +1429,11 @@ int compiled_shapes(int32_t* out, int max_pairs) {
     return n;
 }
 
-hipError_t launch_state(int dk, int dv, int mode, const StepParams& p, int n_states, hipStream_t s) {
-    if (n_states <= 0) return hipSuccess;
-#define SQ_CASE(a, b) if (dk == a && dv == b) return launch_state_t<a, b>(mode, p, n_states, s);
+hipError_t launch_state(int dk, int dv, int mode, const StepParams& p, int n_b, int n_z, hipStream_t s) {
+    if (n_b <= 0 || n_z <= 0 || p.n_heads <= 0) return hipSuccess;
+    if (n_b > 65535 || n_z > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)p.n_heads, (unsigned)n_b, (unsigned)n_z);
+#define SQ_CASE(a, b) if (dk == a && dv == b) return launch_state_t<a, b>(mode, p, grid, s);
     SQ_SHAPES(SQ_CASE)
 #undef SQ_CASE
     return hipErrorInvalidValue;

@@ -10,7 +10,9 @@ namespace sq {
 
 bool shape_compiled(int dk, int dv);
 int compiled_shapes(int32_t* out, int max_pairs);
-hipError_t launch_state(int dk, int dv, int mode, const StepParams& p, int n_states, hipStream_t s);
+// One launch over requests [p.b0, p.b0 + n_b) and layers [p.lz0, p.lz0 + n_z) of the call (relative to
+// p.layer0), every head: a grid of (heads, n_b, n_z) workgroups.
+hipError_t launch_state(int dk, int dv, int mode, const StepParams& p, int n_b, int n_z, hipStream_t s);
 hipError_t launch_codec(int dk, int dv, bool do_export, const CodecParams& p, int n_states, hipStream_t s);
 hipError_t launch_cmp(int dk, int dv, bool int8, int form, int n_heads, int n_slots, int layer0, int n_layers,
                       int batch, const int32_t* slots, int8_t* codes, float* scales, float* S, const float* q,

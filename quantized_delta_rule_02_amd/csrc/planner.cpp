@@ -422,7 +422,7 @@ sq_status build_layout(sq_plan& p) {
     const int GR = gr_of(dv), NG = ng_of(dk, dv);
     p.perm.assign(size_t(LH) * dk, 0);
     p.srow_bits.assign(size_t(LH) * dk, 0);
-    p.srow_w.assign(size_t(LH) * dk, 0.0f);
+    p.srow_wf.assign(size_t(LH) * dk * 2, 0.0f);
     p.grp_bits.assign(size_t(LH) * NG, 0);
     p.grp_off.assign(size_t(LH) * NG, 0);
     p.scale_off.assign(LH, 0);
@@ -439,7 +439,9 @@ sq_status build_layout(sq_plan& p) {
         for (int t = 0; t < dk; ++t) {
             p.perm[size_t(lh) * dk + t] = uint16_t(rows[t]);
             p.srow_bits[size_t(lh) * dk + t] = uint8_t(rb[rows[t]]);
-            p.srow_w[size_t(lh) * dk + t] = p.impact[size_t(lh) * dk + rows[t]];
+            const double w = p.impact[size_t(lh) * dk + rows[t]];
+            p.srow_wf[(size_t(lh) * dk + t) * 2] = float(1.0 / w);
+            p.srow_wf[(size_t(lh) * dk + t) * 2 + 1] = float(std::sqrt(w));
             flags |= (rb[rows[t]] == SQ_PIVOT_BITS) ? kHasPivotRows : kHasCodeRows;
         }
         p.head_flags[lh] = flags;

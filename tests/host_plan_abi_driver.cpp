@@ -14,7 +14,7 @@ bool shape_compiled(int dk, int dv) {
     return (dk == 16 && dv == 16) || (dk == 64 && dv == 64) || (dk == 128 && dv == 128) || (dk == 128 && dv == 256);
 }
 int compiled_shapes(int32_t*, int) { return 4; }
-hipError_t launch_state(int, int, int, const StepParams&, int, hipStream_t) { abort(); }
+hipError_t launch_state(int, int, int, const StepParams&, int, int, hipStream_t) { abort(); }
 hipError_t launch_codec(int, int, bool, const CodecParams&, int, hipStream_t) { abort(); }
 hipError_t launch_cmp(int, int, bool, int, int, int, int, int, int, const int32_t*, int8_t*, float*, float*,
                       const float*, const float*, const float*, const float*, const float*, float*, hipStream_t) { abort(); }
