@@ -717,7 +717,11 @@ k_state(StepParams a) {
     float c_old[CPL];
     if constexpr (kNeedOld) {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) c_old[c] = act ? h2f(rs[DK + col0 + c]) : 1.f;
+        for (int c = 0; c < CPL; ++c) {
+            c_old[c] = act ? h2f(rs[DK + col0 + c]) : 1.f;
+            // converted once here: otherwise each use becomes a mixed-precision FMA, of the slow kind
+            __asm__ volatile("" : "+v"(c_old[c]));
+        }
     }
     int rbits = 16, perm = 0;
     float2 wrow = make_float2(1.f, 1.f);
