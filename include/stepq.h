@@ -149,7 +149,10 @@ sq_status sq_calib_generate(uint64_t seed, int32_t layer, int32_t head, int32_t 
  * device (the pool object owns those small allocations until destroyed); calls
  * on the pool must run with that device current, otherwise SQ_ERR_ARG.  A slot
  * whose bytes are all zero holds the zero state (its scales are 0), so a new
- * request's slot may be cleared instead of imported. */
+ * request's slot may be cleared instead of imported.  Every call below that
+ * takes d_slots skips a request whose slot lies outside [0, n_slots): no pool
+ * byte is touched for it and its outputs keep their previous contents
+ * (sq_state_step with SQ_STEP_VALIDATE returns SQ_ERR_SLOT instead). */
 sq_status sq_pool_bytes(const sq_plan* plan, int32_t n_slots, size_t* bytes);
 sq_status sq_pool_create(const sq_plan* plan, void* d_pool, size_t pool_bytes, int32_t n_slots,
                          sq_pool** out);

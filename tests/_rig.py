@@ -43,23 +43,31 @@ def oracle_unit_bits(wl: Workload, n_layers: int, calib_segments=2, calib_len=32
 
 class Rig:
     def __init__(self, wl: Workload, n_layers: int, batch: int, unit_bits=None, n_slots=None, slots=None,
-                 oplan=None, mode="dual_axis"):
+                 oplan=None, mode="dual_axis", library_calibration=False):
+        """library_calibration: the library's own planner allocates, from the workload's full calibration
+        (its generator, segments and length); otherwise the allocation is unit_bits, or the oracle
+        planner's from a short calibration."""
         import torch
         self.torch = torch
         self.wl = wl
         self.nL, self.B, self.H, self.dk, self.dv = n_layers, batch, wl.n_heads, wl.d_k, wl.d_v
         self.gates = gen.unit_gates(wl)[:n_layers]
         self.impact = gen.impact_scores(wl)[:n_layers]
-        if unit_bits is None:
-            if oplan is None:
-                oplan = oracle_unit_bits(wl, n_layers)
-            unit_bits = oplan.unit_bits
-        self.unit_bits = np.asarray(unit_bits, np.int32)
+        if library_calibration:
+            self.unit_bits = None
+            alloc = dict(calib_seed=gen.calib_seed(wl), calib_segments=wl.calib_segments, calib_len=wl.calib_len)
+        else:
+            if unit_bits is None:
+                if oplan is None:
+                    oplan = oracle_unit_bits(wl, n_layers)
+                unit_bits = oplan.unit_bits
+            self.unit_bits = np.asarray(unit_bits, np.int32)
+            alloc = dict(unit_bits=self.unit_bits)
         self.plan = sq.sq_plan_create(
             form=0 if wl.form == GDN else 1, unit=0 if wl.unit == UNIT_HEAD else 1, n_layers=n_layers,
             n_heads=wl.n_heads, d_k=wl.d_k, d_v=wl.d_v, widths=wl.widths, budget_milli=wl.budget_milli,
-            pivot_ppm=wl.pivot_ppm, grid=wl.grid, gate=self.gates, impact=self.impact, unit_bits=self.unit_bits,
-            quantizer=quant.MODES.index(mode))
+            pivot_ppm=wl.pivot_ppm, grid=wl.grid, gate=self.gates, impact=self.impact,
+            quantizer=quant.MODES.index(mode), **alloc)
         self.mode = mode
         row_bits, w = sq.sq_plan_rows(self.plan)
         self.row_bits = row_bits

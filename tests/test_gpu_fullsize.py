@@ -40,6 +40,7 @@ def _allocation(wl, seed):
 
 
 FULL = [("gdn", configs.GDN_DECODE), ("kda", configs.KDA_DECODE), ("serving6", configs.SERVING_6),
+        ("serving4", configs.SERVING_4), ("serving4-mixed", configs.SERVING_4_MIXED),
         ("outlier", configs.OUTLIER), ("outlier-mixed", configs.OUTLIER_MIXED)]
 
 

@@ -4,12 +4,14 @@ Teacher-forced steps import the oracle's packed state, run one library step,
 export the result and compare it with the oracle's step by the tie-aware rule
 in _parity.py.  Free-running runs compare the final readout and state.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 
 from oracle import quant
 from oracle.numerics import fp16_round
-from oracle.step import packed_step, run_packed
+from oracle.step import packed_step
 from workloads import configs, gen
 
 from _parity import compare_step, step_error_bound
@@ -151,6 +153,35 @@ def test_step_teacher_forced(torch, name, wl, nL, B, T):
         assert R.ok(), f"step {t}: {R.failures}"
         P = P2
     say(name, worst)
+    rig.close()
+
+
+LIBRARY_PLANS = [("gdn", configs.GDN_DECODE, 1, 2, 3), ("kda", configs.KDA_DECODE, 1, 2, 3),
+                 ("serving6", configs.SERVING_6, 2, 1, 2)]
+
+
+@pytest.mark.parametrize("name,wl,nL,B,T", LIBRARY_PLANS, ids=[c[0] for c in LIBRARY_PLANS])
+def test_step_on_the_library_planners_full_plan(torch, name, wl, nL, B, T):
+    """The plan the benchmark steps: the library's planner over the workload's full calibration
+    (32 segments of 512 tokens, its own generator), then teacher-forced steps against the oracle
+    quantizing with that plan's widths, pivots and impact scores."""
+    say(f"library plan {name}: layers={nL} batch={B} steps={T}")
+    rig = _rig(wl, nL, B, library_calibration=True)
+    bits = rig.row_bits
+    assert np.any(bits == 16) and len(np.unique(bits[bits != 16])) >= 2, np.unique(bits)
+    P = quant.quantize(rig.warm_state(), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(T)
+    alpha = rig.alpha_states()
+    for t in range(T):
+        rig.import_packed(P)
+        y_g = rig.step(q[t], k[t], v[t], beta[t])
+        Pg = rig.export_packed()
+        P2, y, X = packed_step(P, rig.rows, q[t], k[t], v[t], alpha, beta[t], wl.grid)
+        R = compare_step(X, y, rig.rows, wl.grid, y_g, Pg, P2,
+                         x_err=step_error_bound(P, rig.rows, k[t], v[t], alpha, beta[t]))
+        assert R.ok(), f"step {t}: {R.failures}"
+        P = P2
+    say(name, R)
     rig.close()
 
 
@@ -443,6 +474,63 @@ def test_split_without_join_per_layer_equals_fused(torch):
     rig.close()
 
 
+SPLIT_CHUNKS = [("one-layer-4-chunks", configs.GDN_DECODE, 1, 33, 40),     # 1056 states: chunks of 9,9,9,6
+                ("three-layers", configs.SERVING_6, 3, 3, 5),               # one chunk per layer
+                ("kda-one-layer-3-chunks", configs.KDA_DECODE, 1, 26, 30)]  # 832 states: chunks of 9,9,8
+
+
+@pytest.mark.parametrize("name,wl,nL,B,n_slots", SPLIT_CHUNKS, ids=[c[0] for c in SPLIT_CHUNKS])
+def test_split_with_several_chunks_is_bitwise_fused(torch, name, wl, nL, B, n_slots):
+    """One split call that the library cuts into several chunks (a readout kernel and a fit + pack
+    kernel per chunk, chained by events): with a second stream, without one, and with long matrix
+    products delaying either stream, two steps give the fused kernel's bytes and readout exactly."""
+    import quantized_delta_rule_02_amd as sq
+    say(f"split with several chunks {name}: {nL} layers x {B} requests")
+    slot_map = np.random.default_rng(8).permutation(n_slots)[:B].astype(np.int32)
+    rig = _rig(wl, nL, B, n_slots=n_slots, slots=slot_map, unit_bits=_fullsize_allocation(wl, nL, 17))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    every = torch.arange(n_slots, dtype=torch.int32, device="cuda")
+    sq.sq_pack(rig.pool, 0, nL, n_slots, every, torch.randn(nL * n_slots * rig.H * rig.dk * rig.dv,
+                                                            device="cuda", generator=g) * 2.0)
+    torch.cuda.synchronize()
+    mem0 = rig.mem.clone()
+    q, k, v, beta = rig.inputs(2)
+    aux = torch.cuda.Stream()
+    big = torch.randn(4096, 4096, device="cuda")
+    sink = torch.empty_like(big)
+
+    def run(flags, s_aux, delay_on):
+        rig.mem.copy_(mem0)
+        torch.cuda.synchronize()
+        ys = []
+        for t in range(2):
+            if delay_on is not None:
+                with torch.cuda.stream(delay_on):
+                    for _ in range(4):
+                        torch.mm(big, big, out=sink)
+            ys.append(rig.step(q[t], k[t], v[t], beta[t], flags=flags, stream_aux=s_aux))
+        return ys, rig.mem.clone()
+
+    ref_ys, ref_mem = run(0, None, None)
+    assert not torch.equal(ref_mem, mem0)
+    for s_aux, delay_on in ((aux, None), (None, None), (aux, aux), (aux, torch.cuda.current_stream())):
+        ys, mem = run(sq.SQ_STEP_SPLIT, s_aux, delay_on)
+        assert all(np.array_equal(a, b) for a, b in zip(ys, ref_ys)), (s_aux is None, delay_on is None)
+        assert torch.equal(mem, ref_mem), (s_aux is None, delay_on is None)
+    rig.close()
+
+
+def _fullsize_allocation(wl, n_layers, seed):
+    """Seeded widths per unit for the first n_layers layers: the candidate widths with a quarter / half /
+    quarter mix and a few pivot units."""
+    g = np.random.default_rng(seed)
+    n = n_layers * wl.n_heads * (1 if wl.unit == "head" else wl.d_k)
+    bits = g.choice(np.asarray(wl.widths, np.int32), size=n, p=[0.25, 0.5, 0.25]).astype(np.int32)
+    bits[g.choice(n, max(1, n // 64), replace=False)] = 16
+    return bits
+
+
 def test_split_from_two_host_threads(torch):
     """Two host threads enqueue split steps on one pool at once, one layer each on streams of their own
     (the library serializes the split arrangement's set-up per pool): bytes and readout equal one fused
@@ -584,55 +672,116 @@ def test_repeated_runs_are_deterministic(torch):
 
 # ---------------------------------------------------------------- free-running drift
 
-def _oracle_fp32_rounded(P0, rows, q, k, v, alpha, beta, grid):
-    """The oracle's packed recurrence with the float state rounded to binary32 before each requantization.
+def _oracle_float32_variant(P0, rows, q, k, v, alpha, beta, grid, variant):
+    """The oracle's packed recurrence with its float state X rounded to binary32 before each
+    requantization (variant 0), and further moved entry by entry by -1, 0 or +1 unit in the last
+    binary32 place drawn from a generator seeded by the variant (variants 1, 2, ...).
 
-    This is the smallest perturbation any float32 implementation makes; its distance from the
-    float64 oracle after many steps is the floor that free-running drift can be held to.
-    """
+    These are float32 evaluations of the same step that differ from each other and from the float64
+    oracle only at float32 rounding level; how far they land from the float64 oracle after many steps
+    is the spread that any float32 implementation's drift is measured against.
+    Returns (y [T, N, d_v], dequantized final state)."""
     from oracle.recurrence import delta_update
+    g = np.random.default_rng(1000 + variant)
     P, ys = P0, []
     for t in range(q.shape[0]):
         X, y = delta_update(quant.dequantize(P, rows), q[t], k[t], v[t], alpha[t], beta[t])
-        P = quant.quantize(X.astype(np.float32).astype(np.float64), rows, grid)
+        X = X.astype(np.float32)
+        if variant > 0:
+            X = X + g.integers(-1, 2, size=X.shape).astype(np.float32) * np.spacing(np.abs(X))
+        P = quant.quantize(X.astype(np.float64), rows, grid)
         ys.append(y)
-    return P, np.stack(ys)
+    return np.stack(ys), quant.dequantize(P, rows)
 
 
-@pytest.mark.parametrize("name,wl,nL,B,T", [("tiny", configs.TINY, 1, 1, 64), ("gdn", configs.GDN_DECODE, 1, 1, 256),
-                                            ("kda", configs.KDA_DECODE, 1, 1, 256)],
-                         ids=["tiny", "gdn", "kda"])
+def _per_seed(a, b, n_seeds):
+    """Relative L2 distance of a from b for each seed's block of states (rows of a and b).  Distances
+    below the per-step tolerance (1e-4) count as 0: there the two trajectories still hold the same
+    codes and differ only by float32 rounding of the readout, which is per-step parity, not drift."""
+    a, b = a.reshape(n_seeds, -1), b.reshape(n_seeds, -1)
+    d = np.linalg.norm(a - b, axis=1) / np.linalg.norm(b, axis=1)
+    return np.where(d < 1e-4, 0.0, d)
+
+
+# Workload slices with eight independent trajectories ("seeds": a layer and request each, with its own
+# warmed-up state and inputs), from the workloads' own recipes with fewer heads.
+DRIFT = [("tiny", replace(configs.TINY, batch=8, n_slots=8), 1, 8, 64),
+         ("gdn", replace(configs.GDN_DECODE, n_heads=4, batch=8, n_slots=8), 1, 8, 256),
+         ("kda", replace(configs.KDA_DECODE, n_heads=4, batch=8, n_slots=8), 1, 8, 256),
+         ("serving6", replace(configs.SERVING_6, n_layers=2, n_heads=4, batch=4, n_slots=4), 2, 4, 256),
+         ("serving4", replace(configs.SERVING_4, n_layers=2, n_heads=4, batch=4, n_slots=4), 2, 4, 256),
+         ("outlier", replace(configs.OUTLIER, n_heads=2, batch=8, n_slots=8), 1, 8, 256)]
+N_VARIANTS = 6
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,wl,nL,B,T", DRIFT, ids=[c[0] for c in DRIFT])
 def test_free_running_drift(torch, name, wl, nL, B, T):
-    """Free-running steps from the same packed start.
+    """Free-running steps from the same packed start, over eight seeds, against the float64 oracle.
 
     Quantization is discontinuous and the dual-axis refit spreads one flipped code over its row, so a
-    single tie decided differently in float32 grows into a trajectory that differs at the level of the
-    quantization noise.  The library must stay within the floor set by the oracle with binary32
-    rounding of X (or within 1e-3 when no tie flips), and its accuracy against the unquantized float
-    recurrence must equal the oracle's.
+    single rounding tie decided differently in float32 grows into a trajectory that differs from the
+    float64 one at the level of the quantization noise.  Relative L2 drift of y and of the state at
+    1e-3 after 256 steps is therefore out of reach for any float32 evaluation: six float32 variants of
+    the oracle itself (binary32 rounding of X, then +-1 ulp moves) land 0.10 - 0.16 from it on the GDN
+    slice.  What is checked instead:
+      1. until the first step at which any code or scale of the library differs from the oracle's,
+         the readout agrees within the per-step tolerance (1e-4 relative L2);
+      2. the library's per-seed drift (y and state) is not larger than the float32 variants': a
+         one-sided Mann-Whitney test over the 8 library and 48 variant drifts keeps p >= 1e-3, and
+         the largest library drift stays within 1.25 x the largest variant drift;
+      3. the library's error against the unquantized float recurrence (all steps) equals the
+         oracle's within 3 x the largest disagreement any float32 variant shows (about 0.03 - 0.15 %
+         on the GDN slice).
     """
+    from concurrent.futures import ThreadPoolExecutor
+    from scipy.stats import mannwhitneyu
     from oracle.recurrence import run_unquantized
-    say(f"drift {name} steps={T}")
+    say(f"drift {name}: {nL} layers x {B} requests x {wl.n_heads} heads, {T} steps")
     rig = _rig(wl, nL, B)
     P0 = quant.quantize(rig.warm_state(), rig.rows, wl.grid)
     q, k, v, beta = rig.inputs(T)
     alpha = np.broadcast_to(rig.alpha_states(), (T,) + rig.alpha_states().shape)
-    rig.import_packed(P0)
-    yg = np.stack([rig.step(q[t], k[t], v[t], beta[t]) for t in range(T)])
-    Pg = rig.export_packed()
-    PT, yo = run_packed(P0, rig.rows, q, k, v, alpha, beta, wl.grid)
-    P32, y32 = _oracle_fp32_rounded(P0, rig.rows, q, k, v, alpha, beta, wl.grid)
-    _, yf = run_unquantized(quant.dequantize(P0, rig.rows), q, k, v, alpha, beta)
+    n_seeds = nL * B
+    with ThreadPoolExecutor(N_VARIANTS + 1) as pool:
+        floor_jobs = [pool.submit(_oracle_float32_variant, P0, rig.rows, q, k, v, alpha, beta, wl.grid, j)
+                      for j in range(N_VARIANTS)]
+        free_job = pool.submit(run_unquantized, quant.dequantize(P0, rig.rows), q, k, v, alpha, beta)
+        # library and float64 oracle in lockstep
+        rig.import_packed(P0)
+        P, yg, yo, first_flip = P0, [], [], None
+        for t in range(T):
+            yg.append(rig.step(q[t], k[t], v[t], beta[t]))
+            P, y, _ = packed_step(P, rig.rows, q[t], k[t], v[t], alpha[t], beta[t], wl.grid)
+            yo.append(y)
+            if first_flip is None:
+                Pg = rig.export_packed()
+                same = all(np.array_equal(getattr(Pg, f), getattr(P, f)) for f in ("Q", "r", "c", "V"))
+                assert np.linalg.norm(yg[-1] - y) <= 1e-4 * np.linalg.norm(y), f"step {t} before any flip"
+                if not same:
+                    first_flip = t
+        Pg = rig.export_packed()
+        floors = [j.result() for j in floor_jobs]
+        _, yf = free_job.result()
+    yg, yo = np.stack(yg), np.stack(yo)
+    Xg, Xo = quant.dequantize(Pg, rig.rows), quant.dequantize(P, rig.rows)
+    lib_y, lib_x = _per_seed(yg[-1], yo[-1], n_seeds), _per_seed(Xg, Xo, n_seeds)
+    flo_y = np.concatenate([_per_seed(yj[-1], yo[-1], n_seeds) for yj, _ in floors])
+    flo_x = np.concatenate([_per_seed(Xj, Xo, n_seeds) for _, Xj in floors])
     rel = lambda a, b: float(np.linalg.norm(a - b) / np.linalg.norm(b))
-    drift = rel(yg[-1], yo[-1])
-    floor = rel(y32[-1], yo[-1])
-    x_drift = rel(quant.dequantize(Pg, rig.rows), quant.dequantize(PT, rig.rows))
-    x_floor = rel(quant.dequantize(P32, rig.rows), quant.dequantize(PT, rig.rows))
-    err_g, err_o = rel(yg, yf), rel(yo, yf)
-    say(f"drift {name}: readout {drift:.3e} (floor {floor:.3e}), state {x_drift:.3e} (floor {x_floor:.3e}); "
-        f"error vs unquantized: library {err_g:.4f} oracle {err_o:.4f}")
-    assert drift <= max(1e-3, 2.0 * floor) and x_drift <= max(1e-3, 2.0 * x_floor)
-    assert abs(err_g - err_o) <= 0.1 * err_o + 1e-6
+    err_o = rel(yo, yf)
+    err_g = rel(yg, yf)
+    agree = [abs(rel(yj, yf) - err_o) / err_o for yj, _ in floors]
+    p_y = mannwhitneyu(lib_y, flo_y, alternative="greater").pvalue
+    p_x = mannwhitneyu(lib_x, flo_x, alternative="greater").pvalue
+    say(f"drift {name}: first flip at step {first_flip}; y drift library {np.round(lib_y, 4)} "
+        f"variants {flo_y.min():.4f}..{flo_y.max():.4f} (p {p_y:.3g}); state drift library "
+        f"{np.round(lib_x, 4)} variants {flo_x.min():.4f}..{flo_x.max():.4f} (p {p_x:.3g}); error vs "
+        f"unquantized library {err_g:.5f} oracle {err_o:.5f} ({abs(err_g - err_o) / err_o:.2e}), variants "
+        f"{min(agree):.2e}..{max(agree):.2e}")
+    assert p_y >= 1e-3 and p_x >= 1e-3
+    assert lib_y.max() <= 1.25 * flo_y.max() and lib_x.max() <= 1.25 * flo_x.max()
+    assert abs(err_g - err_o) <= 3.0 * max(agree) * err_o
     rig.close()
 
 
@@ -771,6 +920,101 @@ def test_validate_mode_rejects_bad_slots(torch):
         with pytest.raises(sq.StepQError) as e:
             rig.step(q[0], k[0], v[0], beta[0], flags=sq.SQ_STEP_VALIDATE)
         assert e.value.status == -4
+    rig.close()
+
+
+def test_out_of_range_slots_are_skipped(torch):
+    """A slot outside [0, n_slots) (too large or negative) is skipped by every kernel without
+    SQ_STEP_VALIDATE: the pool's bytes and that request's outputs stay as they were, and the other
+    request gets exactly what a call without the bad one gives (fused and split step, pack, unpack,
+    export, import, and the INT8 comparator)."""
+    import quantized_delta_rule_02_amd as sq
+    wl = configs.GDN_DECODE
+    say("out-of-range slots gdn")
+    n_slots, H, dk, dv = 4, wl.n_heads, wl.d_k, wl.d_v
+    rig = _rig(wl, 1, 2, n_slots=n_slots)
+    f32 = torch.float32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    sq.sq_pack(rig.pool, 0, 1, n_slots, torch.arange(n_slots, dtype=torch.int32, device="cuda"),
+               torch.randn(n_slots * H * dk * dv, device="cuda", generator=g))
+    q, k, v, beta = rig.inputs(1)
+    t = lambda a: rig._t(np.ascontiguousarray(a).reshape(-1), f32)
+    qs, ks, vs, bs, gate = t(q[0]), t(k[0]), t(v[0]), t(beta[0]), rig.gate_step()
+    X = torch.randn(2 * H * dk * dv, device="cuda", generator=g)
+    torch.cuda.synchronize()
+    mem0 = rig.mem.clone()
+    for bad in (7, -3):
+        pair = torch.tensor([2, bad], dtype=torch.int32, device="cuda")
+        one = pair[:1]
+
+        def both_ways(call):
+            """call(slots, batch) -> list of output tensors; returns (outputs, pool) for the pair and
+            for the good request alone, each from the same starting pool."""
+            res = []
+            for slots, batch in ((pair, 2), (one, 1)):
+                rig.mem.copy_(mem0)
+                outs = call(slots, batch)
+                torch.cuda.synchronize()
+                res.append(([o.clone() for o in outs], rig.mem.clone()))
+            return res
+
+        def step(flags):
+            def call(slots, batch):
+                y = torch.full((2 * H * dv,), 5.0, device="cuda")
+                sq.sq_state_step(rig.pool, 0, 1, batch, slots, qs[:batch * H * dk], ks[:batch * H * dk],
+                                 vs[:batch * H * dv], gate[:batch * H], bs[:batch * H], y[:batch * H * dv],
+                                 flags=flags)
+                return [y]
+            return call
+
+        def pack(slots, batch):
+            sq.sq_pack(rig.pool, 0, 1, batch, slots, X[:batch * H * dk * dv])
+            return []
+
+        def unpack(slots, batch):
+            out = torch.full((2 * H * dk * dv,), 5.0, device="cuda")
+            sq.sq_unpack(rig.pool, 0, 1, batch, slots, out[:batch * H * dk * dv])
+            return [out]
+
+        def export(slots, batch):
+            c = torch.full((2 * H * dk * dv,), 5, dtype=torch.int16, device="cuda")
+            r = torch.full((2 * H * dk,), 5, dtype=torch.int16, device="cuda")
+            cc = torch.full((2 * H * dv,), 5, dtype=torch.int16, device="cuda")
+            sq.sq_export(rig.pool, 0, 1, batch, slots, c[:batch * H * dk * dv], r[:batch * H * dk], cc[:batch * H * dv])
+            return [c, r, cc]
+
+        ex = export(torch.tensor([1, 3], dtype=torch.int32, device="cuda"), 2)
+
+        def imp(slots, batch):
+            sq.sq_import(rig.pool, 0, 1, batch, slots, ex[0][:batch * H * dk * dv], ex[1][:batch * H * dk],
+                         ex[2][:batch * H * dv])
+            return []
+
+        for name, call in (("fused", step(0)), ("split", step(sq.SQ_STEP_SPLIT)), ("pack", pack),
+                           ("unpack", unpack), ("export", export), ("import", imp)):
+            (o2, m2), (o1, m1) = both_ways(call)
+            assert torch.equal(m2, m1), (bad, name)
+            for a, b in zip(o2, o1):
+                assert torch.equal(a, b), (bad, name)
+            if name in ("fused", "unpack", "export"):
+                assert bool((o2[0][o2[0].numel() // 2:] == 5).all()), (bad, name)
+            if name in ("unpack", "export"):
+                assert torch.equal(m2, mem0), (bad, name)
+        # INT8 comparator: codes and scales of every slot, the bad request's readout untouched
+        codes = torch.randint(-127, 128, (n_slots * H * dk * dv,), dtype=torch.int8, device="cuda", generator=g)
+        scales = torch.rand(n_slots * H * dk, device="cuda", generator=g)
+        outs = []
+        for slots, batch in ((pair, 2), (one, 1)):
+            c, s_ = codes.clone(), scales.clone()
+            y = torch.full((2 * H * dv,), 5.0, device="cuda")
+            sq.sq_int8_step(0, H, dk, dv, n_slots, 0, 1, batch, slots, c, s_, qs[:batch * H * dk],
+                            ks[:batch * H * dk], vs[:batch * H * dv], gate[:batch * H], bs[:batch * H],
+                            y[:batch * H * dv])
+            torch.cuda.synchronize()
+            outs.append((c, s_, y))
+        assert all(torch.equal(a, b) for a, b in zip(outs[0], outs[1])), bad
+        assert bool((outs[0][2][H * dv:] == 5).all())
     rig.close()
 
 

@@ -5,6 +5,7 @@ import ctypes
 import json
 import os
 import subprocess
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -71,7 +72,10 @@ CASES = [("tiny", configs.TINY, 1, 2, 16, 0), ("gdn", configs.GDN_DECODE, 1, 2, 
          ("outlier", configs.OUTLIER, 1, 1, 12, 0), ("gdn-row-absmax", configs.GDN_DECODE, 1, 2, 24, 1),
          ("kda-row-absmax", configs.KDA_DECODE, 1, 2, 16, 1),
          ("serving4-mixed", configs.SERVING_4_MIXED, 2, 1, 16, 0), ("outlier-mixed", configs.OUTLIER_MIXED, 1, 1, 12, 0),
-         ("kda64", configs.KDA_64, 1, 2, 16, 0)]
+         ("kda64", configs.KDA_64, 1, 2, 16, 0),
+         # the workloads' full calibration (32 segments of 512 tokens) on two heads
+         ("gdn-2h-full-calibration", replace(configs.GDN_DECODE, n_heads=2), 1, 32, 512, 0),
+         ("kda-2h-full-calibration", replace(configs.KDA_DECODE, n_heads=2), 1, 32, 512, 0)]
 
 
 @pytest.mark.parametrize("name,wl,nL,S,T,qz", CASES, ids=[c[0] for c in CASES])
