@@ -195,6 +195,24 @@ sq_status sq_state_step(sq_pool* pool, int32_t layer0, int32_t n_layers, int32_t
                         const float* d_v, const float* d_gate, const float* d_beta, float* d_y,
                         void* stream_main, void* stream_aux, uint32_t flags);
 
+/* ---- state_step, split, without allocation -----------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * two kernels as sq_state_step with SQ_STEP_SPLIT, both on one stream, with
+ * the scratch e = v - k^T D S in a fixed array of SQ_SPLIT_STATIC_MAX_FLOATS
+ * floats that the library holds on each GPU until the process ends (its
+ * address is looked up when a pool is created on that GPU).  Same arguments
+ * and layouts as sq_state_step; bitwise the same y and pool bytes.
+ * n_layers * batch * H * d_v above the limit: SQ_ERR_ARG, nothing enqueued.
+ * Every call on one GPU uses the same array: calls that overlap on that GPU
+ * (other streams, other host threads, other pools) race and their results
+ * are undefined; order them.  Makes no device allocation and no host copy. */
+#define SQ_SPLIT_STATIC_MAX_FLOATS (8ll << 20)
+sq_status sq_state_step_split_static(sq_pool* pool, int32_t layer0, int32_t n_layers,
+                                     int32_t batch, const int32_t* d_slots, const float* d_q,
+                                     const float* d_k, const float* d_v, const float* d_gate,
+                                     const float* d_beta, float* d_y, void* stream);
+
 /* ---- pack / unpack -----------------------------------------------------
  * sq_pack quantizes float states d_X [n_layers][batch][H][d_k][d_v] into the
  * slots (row factors, column fit, rounding; the requantization half of a

@@ -15,14 +15,15 @@ import numpy as np
 
 from . import _lib
 from ._lib import (SQ_FORM_GDN, SQ_FORM_KDA, SQ_PIVOT_BITS, SQ_QUANT_DUAL_AXIS, SQ_QUANT_ROW_ABSMAX,
-                   SQ_STEP_NO_JOIN, SQ_STEP_SPLIT, SQ_STEP_VALIDATE, SQ_UNIT_HEAD, SQ_UNIT_ROW)
+                   SQ_SPLIT_STATIC_MAX_FLOATS, SQ_STEP_NO_JOIN, SQ_STEP_SPLIT, SQ_STEP_VALIDATE, SQ_UNIT_HEAD,
+                   SQ_UNIT_ROW)
 
 __all__ = [
     "StepQError", "Plan", "Pool", "sq_plan_create", "sq_plan_describe", "sq_plan_info", "sq_pool_bind", "sq_pool_release", "sq_plan_units", "sq_plan_rows",
-    "sq_plan_save", "sq_plan_load", "sq_calib_generate", "sq_pool_bytes", "sq_pool_create", "sq_state_step",
+    "sq_plan_save", "sq_plan_load", "sq_calib_generate", "sq_pool_bytes", "sq_pool_create", "sq_state_step", "sq_state_step_split_static",
     "sq_pack", "sq_unpack", "sq_export", "sq_import", "sq_int8_step", "sq_fp32_step", "sq_copy", "sq_valu_probe",
     "sq_supported_shapes", "SQ_FORM_GDN", "SQ_FORM_KDA", "SQ_UNIT_HEAD", "SQ_UNIT_ROW", "SQ_STEP_SPLIT",
-    "SQ_STEP_VALIDATE", "SQ_STEP_NO_JOIN", "SQ_PIVOT_BITS", "SQ_QUANT_DUAL_AXIS", "SQ_QUANT_ROW_ABSMAX",
+    "SQ_STEP_VALIDATE", "SQ_STEP_NO_JOIN", "SQ_SPLIT_STATIC_MAX_FLOATS", "SQ_PIVOT_BITS", "SQ_QUANT_DUAL_AXIS", "SQ_QUANT_ROW_ABSMAX",
 ]
 
 
@@ -287,6 +288,19 @@ def sq_state_step(pool: Pool, layer0, n_layers, batch, slots, q, k, v, gate, bet
         _dev(q, f, n * pool.d_k, "q"), _dev(k, f, n * pool.d_k, "k"), _dev(v, f, n * pool.d_v, "v"),
         _dev(gate, f, n_gate, "gate"), _dev(beta, f, n, "beta"), _dev(y, f, n * pool.d_v, "y"),
         _stream(stream_main), aux, int(flags)), "sq_state_step")
+
+
+def sq_state_step_split_static(pool: Pool, layer0, n_layers, batch, slots, q, k, v, gate, beta, y, stream=None):
+    """The split step with the library's fixed per-GPU scratch (no device allocation)."""
+    import torch
+    n = n_layers * batch * pool.H
+    f = torch.float32
+    n_gate = n * (pool.d_k if pool.form == SQ_FORM_KDA else 1)
+    _check(_lib.load().sq_state_step_split_static(
+        pool.handle, layer0, n_layers, batch, _dev(slots, torch.int32, batch, "slots"),
+        _dev(q, f, n * pool.d_k, "q"), _dev(k, f, n * pool.d_k, "k"), _dev(v, f, n * pool.d_v, "v"),
+        _dev(gate, f, n_gate, "gate"), _dev(beta, f, n, "beta"), _dev(y, f, n * pool.d_v, "y"),
+        _stream(stream)), "sq_state_step_split_static")
 
 
 def sq_pack(pool: Pool, layer0, n_layers, batch, slots, X, stream=None):

@@ -17,6 +17,7 @@ SQ_QUANT_DUAL_AXIS, SQ_QUANT_ROW_ABSMAX = 0, 1
 SQ_STEP_SPLIT, SQ_STEP_VALIDATE, SQ_STEP_NO_JOIN = 1, 2, 4
 SQ_PIVOT_BITS = 16
 SQ_MAX_WIDTHS, SQ_MAX_GRID = 8, 8
+SQ_SPLIT_STATIC_MAX_FLOATS = 8 << 20
 
 
 class SqPlanCfg(ctypes.Structure):
@@ -65,6 +66,7 @@ _SIGS = {
     "sq_pool_bind": (c_int32, [_P, _P, c_size_t, c_int32, POINTER(c_void_p)]),
     "sq_pool_release": (None, [_P]),
     "sq_state_step": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_uint32]),
+    "sq_state_step_split_static": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sq_pack": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P]),
     "sq_unpack": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P]),
     "sq_export": (c_int32, [_P, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P]),

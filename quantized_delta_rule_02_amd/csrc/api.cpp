@@ -353,6 +353,9 @@ extern "C" sq_status sq_pool_create(const sq_plan* p, void* d_pool, size_t pool_
     pl->slot_bytes = p->slot_bytes;
     hipError_t e = hipGetDevice(&pl->device);
     if (e != hipSuccess) { delete pl; return hip_fail(e, "hipGetDevice"); }
+    float* scr = nullptr;
+    e = static_scratch(&scr);   // set-up of the allocation-free split step's array on this device
+    if (e != hipSuccess) { delete pl; return hip_fail(e, "looking up the fixed split scratch"); }
     sq_status st = SQ_OK;
     if (st == SQ_OK) st = upload(pl, p->rec_off, &pl->t.rec_off);
     if (st == SQ_OK) st = upload(pl, p->grp_off, &pl->t.grp_off);
@@ -497,6 +500,36 @@ extern "C" sq_status sq_state_step(sq_pool* pl, int32_t layer0, int32_t n_layers
         if (e != hipSuccess) return hip_fail(e, "joining the aux stream");
     }
     return SQ_OK;
+}
+
+static_assert(SQ_SPLIT_STATIC_MAX_FLOATS == kStaticScratchFloats, "fixed split scratch size");
+
+extern "C" sq_status sq_state_step_split_static(sq_pool* pl, int32_t layer0, int32_t n_layers, int32_t batch,
+                                                const int32_t* d_slots, const float* d_q, const float* d_k,
+                                                const float* d_v, const float* d_gate, const float* d_beta,
+                                                float* d_y, void* stream) {
+    sq_status st = check_range(pl, layer0, n_layers, batch);
+    if (st != SQ_OK) return st;
+    if (batch == 0 || n_layers == 0) return SQ_OK;   // nothing to do
+    if (!d_slots || !d_q || !d_k || !d_v || !d_gate || !d_beta || !d_y) { set_error("NULL device array"); return SQ_ERR_ARG; }
+    const int64_t need = int64_t(n_layers) * batch * pl->H * pl->dv;
+    if (need > kStaticScratchFloats) {
+        set_error("split scratch of %lld floats (n_layers * batch * H * d_v) above the fixed %lld",
+                  (long long)need, (long long)kStaticScratchFloats);
+        return SQ_ERR_ARG;
+    }
+    float* scr = nullptr;
+    hipError_t e = static_scratch(&scr);   // looked up when the pool was created on this device
+    if (e != hipSuccess) return hip_fail(e, "fixed split scratch");
+    StepParams p = base_params(pl, layer0, n_layers, batch, d_slots);
+    p.q = d_q; p.k = d_k; p.v = d_v; p.gate = d_gate; p.beta = d_beta; p.y = d_y;
+    p.e_buf = scr;                                  // [layer][request][head][d_v] of this call only
+    p.e_layer_stride = int64_t(batch) * pl->H;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    e = launch_state(pl->dk, pl->dv, kModeSplitA, p, batch, n_layers, s);
+    if (e != hipSuccess) return hip_fail(e, "split readout launch");
+    e = launch_state(pl->dk, pl->dv, kModeSplitB, p, batch, n_layers, s);
+    return e == hipSuccess ? SQ_OK : hip_fail(e, "split fit/pack launch");
 }
 
 // ------------------------------------------------------------------ pack / unpack / export / import

@@ -46,6 +46,8 @@ constexpr int ng_of(int dk, int dv) { return dk / gr_of(dv); }             // gr
 inline int group_bytes(int dv, int bits) { return lpr_of(dv) * 2 * bits; }
 
 constexpr int kMaxGrid = 8;
+// floats of the fixed split scratch (32 MiB per GPU) behind the allocation-free split step
+constexpr int64_t kStaticScratchFloats = int64_t(8) << 20;
 
 // Head flags
 constexpr uint8_t kHasCodeRows = 1;

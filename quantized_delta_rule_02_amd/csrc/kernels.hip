@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "launch.h"
 
@@ -1484,6 +1486,32 @@ hipError_t launch_copy(const void* src, void* dst, size_t n_bytes, hipStream_t s
     if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
     k_copy<<<dim3((unsigned)blocks), dim3(kCopyThreads), 0, s>>>(static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fixed split scratch
+// e = v - k^T D S of every state of one allocation-free split call, one copy per GPU for the life of
+// the process.  Host code never passes the array's own name (on the host it is a stand-in, not a
+// device address) but the address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) float scratch[kStaticScratchFloats];
+
+constexpr int kScratchDevices = 64;
+
+hipError_t static_scratch(float** out) {
+    static std::mutex mu;
+    static float* ptr[kScratchDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* d = nullptr;
+        e = hipGetSymbolAddress(&d, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        ptr[dev] = static_cast<float*>(d);
+    }
+    *out = ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace sq

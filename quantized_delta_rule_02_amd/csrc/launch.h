@@ -18,6 +18,9 @@ hipError_t launch_cmp(int dk, int dv, bool int8, int form, int n_heads, int n_sl
                       int batch, const int32_t* slots, int8_t* codes, float* scales, float* S, const float* q,
                       const float* k, const float* v, const float* gate, const float* beta, float* y,
                       hipStream_t s);
+// Device address of the fixed split scratch (kStaticScratchFloats floats) on the current device, looked up
+// once per device and kept; hipErrorInvalidDevice beyond the devices this process can hold.
+hipError_t static_scratch(float** out);
 hipError_t launch_copy(const void* src, void* dst, size_t n_bytes, hipStream_t s);
 // hipErrorNotSupported: the device's LDS cannot cap residency at waves_per_simd workgroups per CU
 hipError_t launch_valu_probe(int waves_per_simd, int n_blocks, float* out, uint64_t* n_fma, int* blocks_per_cu,

@@ -20,6 +20,7 @@ hipError_t launch_cmp(int, int, bool, int, int, int, int, int, int, const int32_
                       const float*, const float*, const float*, const float*, const float*, float*, hipStream_t) { abort(); }
 hipError_t launch_copy(const void*, void*, size_t, hipStream_t) { abort(); }
 hipError_t launch_valu_probe(int, int, float*, uint64_t*, int*, hipStream_t) { abort(); }
+hipError_t static_scratch(float**) { abort(); }
 }
 
 static int fails = 0;
@@ -127,6 +128,11 @@ int main() {
     std::vector<float> q(2 * 3 * 16), k(2 * 3 * 16), v(2 * 3 * 16), be(2 * 3);
     CHECK(sq_calib_generate(5, 0, 1, 2, 3, 16, 16, q.data(), k.data(), v.data(), be.data()) == SQ_OK);
     CHECK(sq_calib_generate(5, -1, 1, 2, 3, 16, 16, q.data(), k.data(), v.data(), be.data()) != SQ_OK);
+    // device entry points refuse a NULL pool before any HIP call
+    CHECK(sq_state_step(nullptr, 0, 1, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, 0) == SQ_ERR_ARG);
+    CHECK(sq_state_step_split_static(nullptr, 0, 1, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, nullptr) == SQ_ERR_ARG);
     std::printf("%s (%d failures)\n", fails ? "FAILED" : "ok", fails);
     return fails ? 1 : 0;
 }

@@ -30,6 +30,21 @@ def test_library_exports_every_declared_function():
     assert set(names) <= exported
 
 
+def test_header_constants_match_the_binding():
+    """Every numeric #define SQ_* in include/stepq.h has the same value in the Python binding."""
+    import re
+    found = 0
+    for line in open(_lib.HEADER):
+        m = re.match(r"#define\s+(SQ_\w+)\s+(.*?)\s*(/\*.*)?$", line)
+        if not m or not hasattr(_lib, m.group(1)):
+            continue
+        expr = re.sub(r"(\d+)(ll|u)\b", r"\1", m.group(2))
+        assert re.fullmatch(r"[-0-9 <()]+", expr), line
+        assert eval(expr) == getattr(_lib, m.group(1)), line
+        found += 1
+    assert found >= 12 and _lib.SQ_SPLIT_STATIC_MAX_FLOATS == 8 << 20
+
+
 def test_alternative_names_are_the_same_calls():
     """sq_plan_info is sq_plan_describe; sq_pool_bind / sq_pool_release validate like sq_pool_create /
     sq_pool_destroy (host checks only, no device memory)."""
