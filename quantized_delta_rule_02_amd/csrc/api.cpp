@@ -310,7 +310,8 @@ extern "C" sq_status sq_pool_bytes(const sq_plan* p, int32_t n_slots, size_t* by
 template <class T>
 static sq_status upload(sq_pool* pl, const std::vector<T>& v, const T** dst) {
     void* d = nullptr;
-    const size_t n = std::max<size_t>(v.size() * sizeof(T), 16);
+    // whole 16-byte units: kernels read byte tables through dword loads
+    const size_t n = (std::max<size_t>(v.size() * sizeof(T), 16) + 15) & ~size_t(15);
     hipError_t e = hipMalloc(&d, n);
     if (e != hipSuccess) { set_error("hipMalloc of %zu bytes: %s", n, hipGetErrorString(e)); return SQ_ERR_NOMEM; }
     pl->owned.push_back(d);

@@ -294,6 +294,7 @@ struct StepSmem {
     float2 acc[DK];    // column-sum coefficients: D_i r_i (k_i, q_i) on code rows, D_i (k_i, q_i) on pivot rows
     float2 upd[DK];    // update: D_i r_i (D_i on pivot rows), beta k_i
     float4 fit[DK];    // requantization: sqrt(w) r_new, -sqrt(w) r_new / 2, 1/2 - qmax, 1 / r_new
+    float ir[DK];      // 1 / r_new, contiguous: four rows per wide read
     float iq[DK];      // 1 / qmax (0 on pivot rows)
     float2 fin[DK];    // final rounding bounds: magic + container bias -/+ qmax
     float rn[DK];      // new binary16 row factor
@@ -505,16 +506,27 @@ __device__ __forceinline__ void round_pack_uniform(const float* X, const float* 
                                                    const uint32_t* goff, int wave, int lane, bool act) {
     constexpr int CPL = Sh::CPL, GR = Sh::GR, RPW = Sh::RPW, GPW = Sh::GPW, LPR = Sh::LPR;
     const float mb = kMagic + (float)bias_of(W);
+    // the rounding bounds of a group's GR rows (two rows per wide broadcast read); the next group's are read
+    // while this group is rounded and packed
+    float4 fb[2][GR / 2];
+#pragma unroll
+    for (int i = 0; i < GR / 2; ++i) fb[0][i] = reinterpret_cast<const float4*>(sm.fin + wave * RPW)[i];
 #pragma unroll
     for (int g = 0; g < GPW; ++g) {
+        if (g + 1 < GPW) {
+#pragma unroll
+            for (int i = 0; i < GR / 2; ++i)
+                fb[(g + 1) % 2][i] = reinterpret_cast<const float4*>(sm.fin + wave * RPW + (g + 1) * GR)[i];
+        }
         uint8_t* gp = rec + ld_const(goff + wave * GPW + g);
         float m[16];
         uint32_t d[4];
 #pragma unroll
         for (int r = 0; r < GR; ++r) {
-            const float2 bd = sm.fin[wave * RPW + g * GR + r];
+            const float4 f4 = fb[g % 2][r / 2];
+            const float lo = (r % 2) ? f4.z : f4.x, hi = (r % 2) ? f4.w : f4.y;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) m[r * CPL + c] = med3(fmaf(X[16 * g + r * CPL + c], ic[c], mb), bd.x, bd.y);
+            for (int c = 0; c < CPL; ++c) m[r * CPL + c] = med3(fmaf(X[16 * g + r * CPL + c], ic[c], mb), lo, hi);
         }
         if constexpr (W == 4) { pack4m(m, d); if (act) store_dw<2>(gp + lane * 8, d); }
         else if constexpr (W == 6) { pack6m(m, d); if (act) store_dw<3>(gp + lane * 12, d); }
@@ -597,7 +609,11 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 const float fr = __builtin_amdgcn_fractf(A[j][c]);
-                E[j][c] = (FREE0 && j == 0) ? fr : fmaxf(A[j][c], fr);
+                // max(a, fract(a)) on the bit patterns: fract(a) >= +0, so a negative a (a negative
+                // integer pattern) yields fract(a), and two non-negative floats order as their
+                // patterns do.  The integer max issues beside the FMAs; the float max does not.
+                E[j][c] = (FREE0 && j == 0) ? fr
+                                            : __int_as_float(max(__float_as_int(A[j][c]), __float_as_int(fr)));
             }
 #pragma unroll
         for (int j = 0; j < KG; ++j)
@@ -667,7 +683,10 @@ k_state(StepParams a) {
     const int col0 = lane * CPL;
     const uint8_t* gbits = a.t.grp_bits + (size_t)lh * NG;
     const uint32_t* goff = a.t.grp_off + (size_t)lh * NG;
-    const int hflags = uniform((int)a.t.head_flags[lh]);   // a byte: no scalar load, a vector load + readfirstlane
+    // the flags byte through a scalar dword load (the table is padded to whole dwords): a vector byte load
+    // plus readfirstlane would make the wave wait for it before issuing the state's loads
+    const int hflags = (int)((ld_const(reinterpret_cast<const uint32_t*>(a.t.head_flags) + (lh >> 2)) >>
+                              (8 * (lh & 3))) & 0xFFu);
 
     // ---- every load of the state is issued here, at most one dependent level deep (the slot, then the
     // record): the packed groups and scales of the record; the plan's tables; the step's inputs, with
@@ -716,25 +735,44 @@ k_state(StepParams a) {
             }
         }
     }
-    float c_old[CPL];
-    if constexpr (kNeedOld) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            c_old[c] = act ? h2f(rs[DK + col0 + c]) : 1.f;
-            // converted once here: otherwise each use becomes a mixed-precision FMA, of the slow kind
-            __asm__ volatile("" : "+v"(c_old[c]));
-        }
-    }
-    int rbits = 16, perm = 0;
+    // the row tables and scales go out in the same batch as the groups, and one empty asm statement
+    // takes every loaded word at once (the float conversions come after it): the wave waits for memory
+    // once per state instead of once per dependent use
+    uint32_t rbits_u = 16u, perm_u = 0u, rold_bits = 0x3C00u;   // binary16 1.0
     float2 wrow = make_float2(1.f, 1.f);
-    float rold = 1.f;
     if (lane < RPW) {
         const size_t t = (size_t)lh * DK + wave * RPW + lane;
-        rbits = a.t.row_bits[t];
+        rbits_u = a.t.row_bits[t];
         wrow = a.t.row_wf[t];
-        perm = a.t.perm[t];
-        if constexpr (kNeedOld) rold = h2f(rs[wave * RPW + lane]);
+        perm_u = a.t.perm[t];
+        if constexpr (kNeedOld) rold_bits = rs[wave * RPW + lane];
     }
+    // the lane's CPL column scales are adjacent binary16 values (4-byte aligned when CPL > 1): one load
+    constexpr int CW = (CPL + 1) / 2;
+    uint32_t cw[CW];
+#pragma unroll
+    for (int i = 0; i < CW; ++i) cw[i] = 0x3C003C00u;
+    if constexpr (kNeedOld) {
+        if (act) {
+            if constexpr (CPL == 1) cw[0] = rs[DK + col0];
+            else {
+#pragma unroll
+                for (int i = 0; i < CW; ++i) cw[i] = reinterpret_cast<const uint32_t*>(rs + DK + col0)[i];
+            }
+        }
+    }
+    __asm__ volatile("" : "+v"(rbits_u), "+v"(perm_u), "+v"(rold_bits), "+v"(wrow.x), "+v"(wrow.y));
+#pragma unroll
+    for (int i = 0; i < CW; ++i) __asm__ volatile("" : "+v"(cw[i]));
+    const int rbits = (int)rbits_u, perm = (int)perm_u;
+    float c_old[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        c_old[c] = kNeedOld ? h2f((cw[c / 2] >> (16 * (c % 2))) & 0xFFFFu) : 1.f;
+        // converted once here: otherwise each use becomes a mixed-precision FMA, of the slow kind
+        if constexpr (kNeedOld) __asm__ volatile("" : "+v"(c_old[c]));
+    }
+    const float rold = h2f(rold_bits);
 
     // ---- phase 0: per-row coefficients of this wave's rows (lane r < RPW takes row wave * RPW + r)
     if constexpr (kUpdate) {
@@ -900,12 +938,22 @@ k_state(StepParams a) {
             for (int c = 0; c < CPL; ++c) ecol[c] = vv[c];
         }
 
-        // ---- phase 2: the updated float state X = D S + beta k e^T in registers
+        // ---- phase 2: the updated float state X = D S + beta k e^T in registers.  The rows' coefficients
+        // come in blocks of RB rows, two rows per wide broadcast read, all of a block issued before its first
+        // use (read one at a time, each would expose the LDS latency to a handful of FMAs).
+        constexpr int RB = RPW < 16 ? RPW : 16;
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const float2 u = sm.upd[wave * RPW + r];
+        for (int r0 = 0; r0 < RPW; r0 += RB) {
+            float4 uv[RB / 2];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) X[r * CPL + c] = fmaf(u.x, X[r * CPL + c], u.y * ecol[c]);
+            for (int i = 0; i < RB / 2; ++i) uv[i] = reinterpret_cast<const float4*>(sm.upd + wave * RPW + r0)[i];
+            __asm__ volatile("" ::: "memory");
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const float ux = (r % 2) ? uv[r / 2].z : uv[r / 2].x, uy = (r % 2) ? uv[r / 2].w : uv[r / 2].y;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) X[(r0 + r) * CPL + c] = fmaf(ux, X[(r0 + r) * CPL + c], uy * ecol[c]);
+            }
         }
     }
 
@@ -936,7 +984,9 @@ k_state(StepParams a) {
                                                   : m * __builtin_amdgcn_rcpf(qmax));
             sm.rn[t] = rn;
             const float sw = piv ? 0.f : wf.y * rn;
-            sm.fit[t] = make_float4(sw, -0.5f * sw, 0.5f - qmax, __builtin_amdgcn_rcpf(rn));
+            const float irn = __builtin_amdgcn_rcpf(rn);
+            sm.fit[t] = make_float4(sw, -0.5f * sw, 0.5f - qmax, irn);
+            sm.ir[t] = irn;
             sm.iq[t] = piv ? 0.f : __builtin_amdgcn_rcpf(qmax);
             // the row's container width: its group's (wave-uniform values, selected per lane)
             int cb = gb[0];
@@ -954,18 +1004,37 @@ k_state(StepParams a) {
         float c0p[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) c0p[c] = 0.f;
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const float ir = sm.fit[wave * RPW + r].w;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) X[r * CPL + c] *= ir;
-        }
+        // the rows' 1 / r_i in blocks of RB rows, four per wide broadcast read, and the groups' width
+        // checks, all issued before the first use
+        constexpr int RB = RPW < 16 ? RPW : 16;
+        bool one_q[GPW];
+        float iq0[GPW];
 #pragma unroll
         for (int g = 0; g < GPW; ++g) {
             const int t0 = wave * RPW + g * GR;
             // rows are sorted by width, so a group whose first and last rows agree has one qmax
-            if (sm.rb[t0] == sm.rb[t0 + GR - 1]) {
-                const float iq = sm.iq[t0];
+            one_q[g] = sm.rb[t0] == sm.rb[t0 + GR - 1];
+            iq0[g] = sm.iq[t0];
+        }
+#pragma unroll
+        for (int r0 = 0; r0 < RPW; r0 += RB) {
+            float4 irv[RB / 4];
+#pragma unroll
+            for (int i = 0; i < RB / 4; ++i) irv[i] = reinterpret_cast<const float4*>(sm.ir + wave * RPW + r0)[i];
+            __asm__ volatile("" ::: "memory");
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const float4 v4 = irv[r / 4];
+                const float ir = (r % 4 == 0) ? v4.x : (r % 4 == 1) ? v4.y : (r % 4 == 2) ? v4.z : v4.w;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) X[(r0 + r) * CPL + c] *= ir;
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) {
+            const int t0 = wave * RPW + g * GR;
+            if (one_q[g]) {
+                const float iq = iq0[g];
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     float mg = 0.f;
