@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--split", action="store_true", help="time the two-stream arrangement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--summarize", metavar="DB", nargs="+",
+                    help="print per-kernel launch durations and counters from rocprofv3 result databases "
+                         "(no GPU is used)")
+    ap.add_argument("--launches", default="last:20",
+                    help="with --summarize: which launches of each kernel, first:N or last:N")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the comparators (INT8 per-row, FP32), the split arrangement, the candidate-grid "
                          "sweep, the 4-bit budgets, the copy reference, the dual-axis outlier pool and the "
@@ -417,8 +422,52 @@ def valu_ceiling(sq, torch, dev):
     return res
 
 
+def summarize(paths, which):
+    """Per-kernel figures from rocprofv3 result databases (sqlite): mean / min / max duration of the chosen
+    launches of each kernel and the mean of each collected counter over the same launches."""
+    import sqlite3
+    mode, n = which.split(":")
+    n = int(n)
+    for path in paths:
+        con = sqlite3.connect(path)
+        cur = con.cursor()
+        kcols = [r[1] for r in cur.execute("PRAGMA table_info(kernels)")]
+        ki = {c: i for i, c in enumerate(kcols)}
+        name_c = next(c for c in ("kernel_name", "name") if c in ki)
+        disp_c = next(c for c in ("dispatch_id", "id") if c in ki)
+        launches = {}
+        for r in cur.execute("SELECT * FROM kernels ORDER BY start"):
+            launches.setdefault(str(r[ki[name_c]]), []).append((r[ki[disp_c]], r[ki["end"]] - r[ki["start"]]))
+        counters = {}
+        try:
+            ccols = [r[1] for r in cur.execute("PRAGMA table_info(counters_collection)")]
+            ci = {c: i for i, c in enumerate(ccols)}
+            cname = next(c for c in ("counter_name", "name") if c in ci)
+            cval = next(c for c in ("value", "counter_value") if c in ci)
+            for r in cur.execute("SELECT * FROM counters_collection"):
+                key = (r[ci["dispatch_id"]], r[ci[cname]])
+                counters[key] = counters.get(key, 0.0) + float(r[ci[cval]])
+        except Exception:
+            pass
+        cnames = sorted({k[1] for k in counters})
+        print(f"# {path}: {mode} {n} launches of each kernel")
+        print(f"{'kernel':44s} {'calls':>6s} {'used':>5s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"
+              + "".join(f" {c:>18s}" for c in cnames))
+        for name, ls in sorted(launches.items()):
+            sel = ls[:n] if mode == "first" else ls[-n:]
+            d = [x[1] / 1000.0 for x in sel]
+            row = f"{name[:44]:44s} {len(ls):6d} {len(sel):5d} {sum(d) / len(d):10.1f} {min(d):10.1f} {max(d):10.1f}"
+            for c in cnames:
+                vals = [counters[(x[0], c)] for x in sel if (x[0], c) in counters]
+                row += f" {sum(vals) / len(vals):18.6g}" if vals else f" {'-':>18s}"
+            print(row)
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.launches)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the step has no cross-GPU exchange "
               f"and each GPU's share is the single-GPU workload", file=sys.stderr)

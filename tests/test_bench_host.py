@@ -57,3 +57,30 @@ def test_counter_summary_needs_the_matching_kernel_source(tmp_path):
     assert bench._profile_value(str(f), "hbm_bytes_per_launch") == 123.0
     assert bench._profile_value(str(f), "missing") is None
     assert bench._profile_value(str(tmp_path / "absent.txt"), "hbm_bytes_per_launch") is None
+
+
+def test_summarize_reads_a_rocprofv3_database(tmp_path, capsys):
+    """bench.py --summarize: durations and counters of the chosen launches of each kernel, from a database
+    laid out like rocprofv3's (a kernels view with name, dispatch, start and end; counters per dispatch)."""
+    import sqlite3
+    import bench
+    db = str(tmp_path / "run_results.db")
+    con = sqlite3.connect(db)
+    con.execute("CREATE TABLE kernels (dispatch_id INTEGER, kernel_name TEXT, start INTEGER, end INTEGER)")
+    con.execute("CREATE TABLE counters_collection (dispatch_id INTEGER, counter_name TEXT, value REAL)")
+    for i in range(5):   # k_state: 1000, 2000, ... ns; one other kernel
+        con.execute("INSERT INTO kernels VALUES (?, 'sq::k_state<128, 128, 0, 4, false>', ?, ?)",
+                    (i, 10 * i * 1000, 10 * i * 1000 + 1000 * (i + 1)))
+        con.execute("INSERT INTO counters_collection VALUES (?, 'SQ_WAVES', ?)", (i, 100.0 * (i + 1)))
+    con.execute("INSERT INTO kernels VALUES (9, 'sq::k_copy', 0, 500)")
+    con.commit()
+    con.close()
+    bench.summarize([db], "last:2")
+    out = capsys.readouterr().out.splitlines()
+    row = next(l for l in out if l.startswith("sq::k_state"))
+    f = row.split()
+    # last two launches: 4 and 5 us, SQ_WAVES 400 and 500
+    assert "4.5" in f and "4.0" in f and "5.0" in f and "450" in f
+    bench.summarize([db], "first:1")
+    row = next(l for l in capsys.readouterr().out.splitlines() if l.startswith("sq::k_state"))
+    assert "1.0" in row.split() and "100" in row.split()
