@@ -637,8 +637,12 @@ def main():
             torch.cuda.synchronize()
             if i >= args.warmup:
                 t_y += a0.elapsed_time(a1)
+        # the same two kernels per layer on one stream: readout (A) and fit + pack (B) never overlap, so the
+        # sum is their cost without the streams' competition for the CUs
+        ms1 = time_calls(lambda: sq.sq_state_step(pool, 0, L, B, slots, q1, k1, v1, gate, b1, y,
+                                                  flags=sq.SQ_STEP_SPLIT), args.steps)
         extras["split2"] = {"ms": mss, "state_updates_per_s": per_step / (mss / 1e3),
-                            "time_to_y_ms": t_y / args.steps}
+                            "time_to_y_ms": t_y / args.steps, "one_stream_ms": ms1}
         # candidate-grid sweep on the same packed pool (the grid does not change the layout)
         units = sq.sq_plan_units(plan)["unit_bits"]
         sweep = {}
