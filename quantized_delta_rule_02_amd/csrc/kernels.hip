@@ -837,6 +837,32 @@ k_state(StepParams a) {
             unpack_acc_uniform<NARROW ? 2 : 4, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act, c_old);
         else if (NARROW && same && gb[0] == 3)
             unpack_acc_uniform<NARROW ? 3 : 4, kAccum, Sh>(raw, X, sm, wave, U1, P1, rec, goff, lane, act, c_old);
+        else if (same && gb[0] == 16) {
+            // four 16-bit groups (a pivot head, or groups promoted by a pivot row): straight-line, with every
+            // group's second half loaded first (through the per-group branches below these spill)
+            uint32_t hi[GPW][4];
+#pragma unroll
+            for (int g = 0; g < GPW; ++g) {
+                if (act) load_dw<4>(rec + ld_const(goff + wave * GPW + g) + lane * 32 + 16, hi[g]);
+                else hi[g][0] = hi[g][1] = hi[g][2] = hi[g][3] = 0;
+            }
+            const bool all_pivot = !(hflags & kHasCodeRows);
+#pragma unroll
+            for (int g = 0; g < GPW; ++g) {
+                float* xg = &X[16 * g];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t w = e < 8 ? raw[g][e >> 1] : hi[g][(e - 8) >> 1];
+                    const uint32_t bits = (w >> (16 * (e & 1))) & 0xFFFFu;
+                    if (all_pivot) xg[e] = h2f(bits);
+                    else {
+                        const int t = wave * RPW + (16 * g + e) / CPL;
+                        xg[e] = (sm.rb[t] == 16) ? h2f(bits) : c_old[e % CPL] * (float)(int16_t)bits;
+                    }
+                }
+                acc_group<kAccum, Sh>(sm, wave, g, xg, U1, P1);
+            }
+        }
         else
 #pragma unroll
         for (int g = 0; g < GPW; ++g) {
@@ -1104,6 +1130,18 @@ k_state(StepParams a) {
     else if (same6 && gb[0] == 8) round_pack_uniform<8, Sh>(X, ic, sm, rec, goff, wave, lane, act);
     else if (NARROW && same6 && gb[0] == 2) round_pack_uniform<NARROW ? 2 : 4, Sh>(X, ic, sm, rec, goff, wave, lane, act);
     else if (NARROW && same6 && gb[0] == 3) round_pack_uniform<NARROW ? 3 : 4, Sh>(X, ic, sm, rec, goff, wave, lane, act);
+    else if (same6 && gb[0] == 16 && !(hflags & kHasCodeRows)) {
+        // a pivot head: every value stored as binary16, nothing to round to a code
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) {
+            uint32_t d[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                d[i] = __builtin_amdgcn_perm(f2h_bits(fminf(fmaxf(X[16 * g + 2 * i + 1], -65504.f), 65504.f)),
+                                             f2h_bits(fminf(fmaxf(X[16 * g + 2 * i], -65504.f), 65504.f)), 0x05040100u);
+            if (act) store_dw<8>(rec + ld_const(goff + wave * GPW + g) + lane * 32, d);
+        }
+    }
     else
 #pragma unroll
     for (int g = 0; g < GPW; ++g) {
