@@ -576,6 +576,7 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
             Fp[j][c] = 0.f;
         }
     }
+    __builtin_amdgcn_s_setprio(0);   // the row loop at low priority (the kernel's note on wave priority)
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
         // two rows at a time: an empty asm "redefines" the inverse scales, so later rows' candidate
@@ -627,6 +628,7 @@ __device__ __forceinline__ void grid_round(Smem& sm, const float* X, const float
                 Fp[j][c] = fmaf(ew, ew, Fp[j][c]);
             }
     }
+    __builtin_amdgcn_s_setprio(3);   // back to high before the round's barrier and reduction
     if (act) {
 #pragma unroll
         for (int j = 0; j < KG; ++j)
@@ -670,13 +672,11 @@ k_state(StepParams a) {
     const int b = a.b0 + block_idy();
     const int lz = a.lz0 + block_idz();
     const int sid = (lz * a.batch + b) * a.n_heads + h;   // index of the state in the call's input arrays
-    // Wave priority: high outside the column fit, low inside it, when the fit is one round of at most four
-    // waves.  The other phases are chains of dependent loads, LDS round trips and barriers, the fit is long
-    // independent FMA chains; with the SIMD's arbiter preferring the latency-bound waves, the fit's waves
-    // fill the gaps instead of delaying them.  With the fit split into rounds separated by barriers (eight
-    // waves, or more candidates than one round holds) a low-priority fit only stretches those barriers.
-    const bool fit_low = NW <= 4 && a.n_grid <= KG;
-    if (fit_low) __builtin_amdgcn_s_setprio(3);
+    // Wave priority: high, except over the column fit's row loops (grid_round).  The other phases are chains
+    // of dependent loads, LDS round trips and barriers, the row loops are long independent FMA chains; with
+    // the SIMD's arbiter preferring the latency-bound waves, the fit's waves fill the gaps instead of
+    // delaying them.
+    __builtin_amdgcn_s_setprio(3);
     const int lh = (a.layer0 + lz) * a.n_heads + h;
     // per-state table values are the same for every lane: scalar loads, kept in scalar registers so
     // that the width dispatch below is a uniform branch
@@ -1098,7 +1098,6 @@ k_state(StepParams a) {
         }
     }
 
-    if (fit_low) __builtin_amdgcn_s_setprio(0);
     // ---- phase 5: column fit over the candidate grid, KG candidates per LDS round
     float cbest[CPL], fbest[CPL];
 #pragma unroll
@@ -1129,7 +1128,6 @@ k_state(StepParams a) {
         ic[c] = __builtin_amdgcn_rcpf(cbest[c]);
     }
 
-    if (fit_low) __builtin_amdgcn_s_setprio(3);
     // ---- phase 6: round (magic-number RNE + clamp), pack and write back codes, row factors, column scales
     bool same6 = true;
 #pragma unroll
