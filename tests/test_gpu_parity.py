@@ -185,6 +185,36 @@ def test_step_on_the_library_planners_full_plan(torch, name, wl, nL, B, T):
     rig.close()
 
 
+@pytest.mark.parametrize("n_piv", [28, 32], ids=["pivot-and-code-rows", "all-pivot-band"])
+def test_wave_of_sixteen_bit_groups(torch, n_piv):
+    """A KDA head whose first n_piv key rows are pivots: the first wave's four 8-row groups all use 16-bit
+    containers -- with 28 pivots the last of them holds four pivot rows and four code rows (stored as int16
+    codes), with 32 every row of the wave is a pivot -- while the head's other waves hold codes.  Teacher-forced
+    steps against the oracle."""
+    wl = configs.KDA_DECODE
+    B, T = 2, 3
+    say(f"wave of 16-bit groups, {n_piv} pivot rows")
+    bits = np.full((1, wl.n_heads, wl.d_k), 6, np.int32)
+    bits[0, 0, :n_piv] = 16
+    bits[0, 1, :3] = 16
+    rig = _rig(wl, 1, B, unit_bits=bits.reshape(-1))
+    rb = rig.row_bits
+    assert int(np.sum(rb[0, 0] == 16)) == n_piv
+    P = quant.quantize(rig.warm_state(steps=64), rig.rows, wl.grid)
+    q, k, v, beta = rig.inputs(T)
+    alpha = rig.alpha_states()
+    for t in range(T):
+        rig.import_packed(P)
+        y_g = rig.step(q[t], k[t], v[t], beta[t])
+        Pg = rig.export_packed()
+        P2, y, X = packed_step(P, rig.rows, q[t], k[t], v[t], alpha, beta[t], wl.grid)
+        R = compare_step(X, y, rig.rows, wl.grid, y_g, Pg, P2,
+                         x_err=step_error_bound(P, rig.rows, k[t], v[t], alpha, beta[t]))
+        assert R.ok(), f"step {t}: {R.failures}"
+        P = P2
+    rig.close()
+
+
 def _degenerate_states(rig, seed):
     """Float states with the method's special cases, one per state index; the rest random."""
     g = np.random.default_rng(seed)
